@@ -1,0 +1,149 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 int4 weight-only linear layer.
+ *
+ * The operation (LLM170, CUDA/W4A16 page, opening description): weights are
+ * int4, symmetric (no zero point), with one fp16 scale per group of `group`
+ * input features along K (128 for the dense model, 32 for the MoE models);
+ * activations and outputs are IEEE binary16.  For x [M, K], packed weights of
+ * W [N, K] and scales s [N, K/group]:
+ *
+ *     y[m, n] = sum_k x[m, k] * s[n, k / group] * q[n, k],   q in [-8, 7]
+ *
+ * accumulated in fp32 and rounded once to fp16 (round to nearest even).
+ *
+ * Storage (the reading this library fixes; the pages name only "int4 sym"):
+ *   - code q is stored as the offset-binary nibble u = q + 8 (0..15);
+ *   - eight nibbles per uint32 along K: element k = 8j + i of a row lives in
+ *     bits [4i, 4i+4) of word j (low nibble first);
+ *   - packed weights: uint32 [N, K/8] row-major (row n = output feature n);
+ *   - scales: fp16 [N, K/group] row-major;
+ *   - x: fp16 [M, K] row-major; y: fp16 [M, N] row-major;
+ *   - MoE banks: packed uint32 [E, N, K/8], scales fp16 [E, N, K/group].
+ * fp16 values cross the ABI as uint16_t bit patterns.
+ *
+ * Conventions for every entry point:
+ *   - Every return value is a w4a16_status; nothing throws, aborts or prints.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation error no output is written.
+ *   - m == 0, n == 0 or rows == 0 is a successful no-op.
+ *   - The caller owns every buffer.  Device entry points take device pointers,
+ *     run asynchronously on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise; host entry points take host pointers and
+ *     are synchronous.
+ *   - Alignment: x, y and packed weights 16-byte aligned, scales 2-byte
+ *     aligned, offsets 4-byte aligned; K must be a multiple of `group`, and
+ *     `group` must be 32 or 128 (the two sizes the pages name).
+ *   - Calls on different streams may run concurrently; outputs must not alias
+ *     inputs.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_NULL = 1,      /* a required pointer is NULL */
+  W4A16_ERR_SHAPE = 2,     /* negative or inconsistent sizes, K % group != 0, M out of range */
+  W4A16_ERR_GROUP = 3,     /* group size not in {32, 128} */
+  W4A16_ERR_ALIGN = 4,     /* a pointer violates the alignment rules above */
+  W4A16_ERR_WORKSPACE = 5, /* workspace missing or smaller than the query says */
+  W4A16_ERR_HIP = 6,       /* the HIP runtime reported an error (launch or device query) */
+  W4A16_ERR_RANGE = 7      /* a value is out of range: a code outside [-8,7], a non-finite
+                              weight, or a group scale that overflows fp16 */
+} w4a16_status;
+
+/* Version of this ABI (W4A16_ABI_VERSION). */
+int w4a16_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* w4a16_status_str(int status);
+
+/* ---------------------------------------------------------------- host ---- */
+
+/*
+ * Quantise fp32 weights w [n, k] (host) to packed codes (host, uint32 [n, k/8])
+ * and fp16 scales (host, uint16 bits [n, k/group]).  Per group of `group`
+ * consecutive k in a row: a = max |w| (fp32); s = fp16(a / 7) with the divide
+ * in fp32 and round-to-nearest-even into fp16; q = clamp(rint(w / s), -8, 7)
+ * with the divide in fp32 and ties to even; a group whose s is 0 gets q = 0.
+ * Errors: NULL pointers, bad shapes/group, W4A16_ERR_RANGE for a non-finite w
+ * or an s that overflows fp16 (nothing is written then).
+ */
+int w4a16_quantize(const float* w, int64_t n, int64_t k, int32_t group,
+                   uint32_t* packed, uint16_t* scales);
+
+/*
+ * Pack int8 codes q [n, k] (host, each in [-8, 7]) into uint32 [n, k/8] (host).
+ * k must be a multiple of 8.  W4A16_ERR_RANGE if a code is out of range.
+ */
+int w4a16_pack(const int8_t* q, int64_t n, int64_t k, uint32_t* packed);
+
+/* Unpack uint32 [n, k/8] (host) back to int8 codes q [n, k] (host). */
+int w4a16_unpack(const uint32_t* packed, int64_t n, int64_t k, int8_t* q);
+
+/* -------------------------------------------------------------- device ---- */
+
+/*
+ * Decode GEMV, 1 <= m <= 4 (the M = 1 decode step and the batched np4 decode
+ * of the LLM170 CUDA/W4A16 page's benchmark tables): y = x . deq(W)^T.
+ * All m rows share one pass over the packed weights.  x [m, k] and y [m, n]
+ * fp16, packed [n, k/8], scales [n, k/group], all on the device.
+ * The activations are staged in on-chip memory (LDS), which bounds k:
+ * W4A16_ERR_SHAPE if k > w4a16_gemv_max_k(m) (w4a16_gemm takes any size).
+ */
+int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+               uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
+               void* stream);
+
+/* Largest k w4a16_gemv accepts for m rows on the current device (0 if m is
+ * outside 1..4 or no device is usable). */
+int64_t w4a16_gemv_max_k(int64_t m);
+
+/*
+ * Bytes of device workspace w4a16_gemm needs for this problem on the current
+ * device (0 means none; the pointer may then be NULL).  Returns 0 for invalid
+ * shapes as well; w4a16_gemm reports those.
+ */
+size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group);
+
+/*
+ * Prefill GEMM, any m >= 1 (the pp512 / pp4096 prefill of the same tables):
+ * y = x . deq(W)^T with fp16 MFMA and fp32 accumulation.  Same layouts as
+ * w4a16_gemv.  `workspace` (device, at least w4a16_gemm_workspace_bytes)
+ * holds the partial tiles of the split-K schedule; the library leaves it in
+ * the state it needs for the next call, so a buffer may be reused by calls
+ * that run one after another on the same stream, but not by concurrent ones.
+ * A fresh workspace must be zero-filled once before its first use.
+ */
+int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+               uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MoE grouped GEMM (the routed-expert layers of the 35B-A3B MoE model on the
+ * LLM170 CUDA/W4A16 page, g32).  x [rows, k] holds one row per (token, expert)
+ * pair, sorted by expert; rows offsets[e] .. offsets[e+1]-1 belong to expert e
+ * (offsets: device int32 [num_experts + 1], non-decreasing, offsets[0] = 0,
+ * offsets[num_experts] = rows -- a precondition that is not checked, since
+ * checking it would need a device-to-host copy).  packed [E, n, k/8] and
+ * scales [E, n, k/group] hold the experts' weights.  y [rows, n]: row r is
+ * x[r] . deq(W_e)^T for the expert e that owns row r.  No combine across
+ * experts is done.
+ */
+int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                       const int32_t* offsets, uint16_t* y, int32_t num_experts,
+                       int64_t rows, int64_t n, int64_t k, int32_t group, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,184 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared
+symbol, its host quantiser and packing match the oracle bit for bit, and every
+validation error is reported before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w4a16_int4_weight_linear_amd as w4
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "w4a16.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(w4.lib, name), name           # dlsym succeeds
+        assert name in w4.SIGNATURES, name           # the binding knows its signature
+    assert set(w4.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings():
+    assert w4.lib.w4a16_abi_version() == 1
+    for s in range(8):
+        assert w4.lib.w4a16_status_str(s).decode().startswith("W4A16_")
+    assert b"unknown" in w4.lib.w4a16_status_str(99)
+
+
+# ---------------------------------------------------------------------------
+# Host quantiser / packing: bit-exact against the oracle.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("group", [32, 128])
+def test_quantize_matches_oracle_bit_exact(group):
+    rng = np.random.default_rng(100 + group)
+    w = synth.weights(rng, 96, 8 * group)
+    w[0, :group] = 0                                    # zero group
+    w[1, group:2 * group] *= 1e-7                       # tiny / subnormal scales
+    w[2, :group] *= 3e3                                 # large scales
+    w[3, :group] = np.float32(0.25)                     # constant group
+    p, s = w4.quantize(w, group)
+    q_ref, s_ref = oracle.quantize(w, group)
+    assert np.array_equal(s.view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(p, oracle.pack(q_ref))
+
+
+def test_quantize_golden_groups():
+    import test_oracle_pins as pins
+    for g in pins.read_quant_groups():
+        w = np.zeros((1, 32), np.float32)
+        w[0, : len(g["w"])] = g["w"]
+        p, s = w4.quantize(w, 32)
+        assert int(s.view(np.uint16)[0, 0]) == g["scale_bits"], g["name"]
+        want = np.zeros((1, 32), np.int8)
+        want[0, : len(g["q"])] = g["q"]
+        assert np.array_equal(w4.unpack(p, 32), want), g["name"]
+
+
+def test_scale_rounding_over_many_magnitudes():
+    """The C++ fp32->fp16 rounding of a/7 agrees with numpy across the fp16 range."""
+    rng = np.random.default_rng(101)
+    e = rng.uniform(-30, 18, size=4000)
+    a = (np.exp2(e) * rng.uniform(1, 2, size=e.size)).astype(np.float32)
+    w = np.zeros((a.size, 32), np.float32)
+    w[:, 5] = a
+    w[:, 9] = -a * np.float32(0.37)
+    with np.errstate(over="ignore"):
+        keep = (a / np.float32(7)).astype(np.float16) < np.float16(np.inf)
+    w = w[keep]
+    p, s = w4.quantize(w, 32)
+    q_ref, s_ref = oracle.quantize(w, 32)
+    assert np.array_equal(s.view(np.uint16), s_ref.view(np.uint16))
+    assert np.array_equal(p, oracle.pack(q_ref))
+
+
+def test_quantize_errors_write_nothing():
+    w = np.ones((2, 32), np.float32)
+    w[1, 3] = np.nan
+    packed = np.full((2, 4), 0xDEADBEEF, np.uint32)
+    scales = np.full((2, 1), 7, np.uint16)
+    st = w4.lib.w4a16_quantize(w.ctypes.data, 2, 32, 32, packed.ctypes.data, scales.ctypes.data)
+    assert st == w4.ERR_RANGE
+    assert np.all(packed == 0xDEADBEEF) and np.all(scales == 7)
+    w = np.full((1, 32), 1e6, np.float32)               # 1e6 / 7 overflows fp16
+    assert w4.lib.w4a16_quantize(w.ctypes.data, 1, 32, 32, packed.ctypes.data, scales.ctypes.data) == w4.ERR_RANGE
+    assert w4.lib.w4a16_quantize(w.ctypes.data, 1, 32, 64, packed.ctypes.data, scales.ctypes.data) == w4.ERR_GROUP
+    assert w4.lib.w4a16_quantize(w.ctypes.data, 1, 48, 32, packed.ctypes.data, scales.ctypes.data) == w4.ERR_SHAPE
+    assert w4.lib.w4a16_quantize(None, 1, 32, 32, packed.ctypes.data, scales.ctypes.data) == w4.ERR_NULL
+    assert w4.lib.w4a16_quantize(None, 0, 32, 32, None, None) == w4.OK
+
+
+def test_pack_unpack_match_oracle():
+    rng = np.random.default_rng(102)
+    q = synth.integer_codes(rng, 50, 256)
+    p = w4.pack(q)
+    assert np.array_equal(p, oracle.pack(q))
+    assert np.array_equal(w4.unpack(p, 256), q)
+    words = rng.integers(0, 2 ** 32, size=(64, 100), dtype=np.uint64).astype(np.uint32)
+    assert np.array_equal(w4.unpack(words, 800), oracle.unpack(words))
+    import test_oracle_pins as pins
+    for codes, word in pins.read_pack_words():
+        assert int(w4.pack(np.array([codes], np.int8))[0, 0]) == word
+
+
+def test_pack_errors():
+    q = np.zeros((1, 8), np.int8)
+    q[0, 2] = 8
+    out = np.zeros((1, 1), np.uint32)
+    assert w4.lib.w4a16_pack(q.ctypes.data, 1, 8, out.ctypes.data) == w4.ERR_RANGE
+    q[0, 2] = -9
+    assert w4.lib.w4a16_pack(q.ctypes.data, 1, 8, out.ctypes.data) == w4.ERR_RANGE
+    assert w4.lib.w4a16_pack(q.ctypes.data, 1, 12, out.ctypes.data) == w4.ERR_SHAPE
+    assert w4.lib.w4a16_pack(None, 1, 8, out.ctypes.data) == w4.ERR_NULL
+    assert w4.lib.w4a16_unpack(None, 1, 8, q.ctypes.data) == w4.ERR_NULL
+    assert w4.lib.w4a16_unpack(out.ctypes.data, -1, 8, q.ctypes.data) == w4.ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# Device entry points: validation runs before any HIP call, so these need no GPU.
+# ---------------------------------------------------------------------------
+A = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+
+
+def test_gemv_validation():
+    g = w4.lib.w4a16_gemv
+    assert g(A, A, A, A, 1, 64, 128, 64, None) == w4.ERR_GROUP
+    assert g(A, A, A, A, 1, 64, 100, 32, None) == w4.ERR_SHAPE
+    assert g(A, A, A, A, 5, 64, 128, 128, None) == w4.ERR_SHAPE
+    assert g(A, A, A, A, -1, 64, 128, 128, None) == w4.ERR_SHAPE
+    assert g(A, A, A, A, 1, -64, 128, 128, None) == w4.ERR_SHAPE
+    assert g(A, A, A, None, 1, 64, 128, 128, None) == w4.ERR_NULL
+    assert g(None, A, A, A, 1, 64, 128, 128, None) == w4.ERR_NULL
+    assert g(A, None, A, A, 1, 64, 128, 128, None) == w4.ERR_NULL
+    assert g(A, A, None, A, 1, 64, 128, 128, None) == w4.ERR_NULL
+    assert g(A + 8, A, A, A, 1, 64, 128, 128, None) == w4.ERR_ALIGN
+    assert g(A, A + 4, A, A, 1, 64, 128, 128, None) == w4.ERR_ALIGN
+    assert g(A, A, A + 1, A, 1, 64, 128, 128, None) == w4.ERR_ALIGN
+    assert g(A, A, A, A + 2, 1, 64, 128, 128, None) == w4.ERR_ALIGN
+    assert g(A, A, A, A, 1, 1 << 22, 1 << 12, 128, None) == w4.ERR_SHAPE   # > 2 GiB of packed weights
+    # empty problems succeed without touching anything
+    assert g(None, None, None, None, 0, 64, 128, 128, None) == w4.OK
+    assert g(None, None, None, None, 1, 0, 128, 128, None) == w4.OK
+    assert w4.lib.w4a16_gemv_max_k(0) == 0 and w4.lib.w4a16_gemv_max_k(5) == 0
+
+
+def test_gemm_validation():
+    g = w4.lib.w4a16_gemm
+    assert g(A, A, A, A, 8, 64, 128, 16, A, 0, None) == w4.ERR_GROUP
+    assert g(A, A, A, A, 8, 64, 96, 128, A, 0, None) == w4.ERR_SHAPE
+    assert g(A, A, A, None, 8, 64, 128, 128, A, 0, None) == w4.ERR_NULL
+    assert g(A, A, A, A + 8, 8, 64, 128, 128, A, 0, None) == w4.ERR_ALIGN
+    assert g(A, A, A, A, 8, 64, 128, 128, A + 4, 0, None) == w4.ERR_ALIGN
+    assert g(None, None, None, None, 0, 64, 128, 128, None, 0, None) == w4.OK
+    assert w4.lib.w4a16_gemm_workspace_bytes(8, 64, 100, 32) == 0
+
+
+def test_grouped_validation():
+    g = w4.lib.w4a16_grouped_gemm
+    assert g(A, A, A, A, A, 4, 16, 64, 128, 48, None) == w4.ERR_GROUP
+    assert g(A, A, A, A, A, 4, 16, 64, 100, 32, None) == w4.ERR_SHAPE
+    assert g(A, A, A, A, A, -1, 16, 64, 128, 32, None) == w4.ERR_SHAPE
+    assert g(A, A, A, A, A, 0, 16, 64, 128, 32, None) == w4.ERR_SHAPE
+    assert g(A, A, A, None, A, 4, 16, 64, 128, 32, None) == w4.ERR_NULL
+    assert g(A, A, A, A, None, 4, 16, 64, 128, 32, None) == w4.ERR_NULL
+    assert g(A, A, A, A + 2, A, 4, 16, 64, 128, 32, None) == w4.ERR_ALIGN
+    assert g(A, A, A, A, A + 2, 4, 16, 64, 128, 32, None) == w4.ERR_ALIGN
+    assert g(None, None, None, None, None, 4, 0, 64, 128, 32, None) == w4.OK
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.quantize(np.ones((1, 48), np.float32), 32)
+    assert e.value.status == w4.ERR_SHAPE

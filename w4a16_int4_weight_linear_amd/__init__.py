@@ -1,0 +1,169 @@
+"""Python binding of the gfx950 W4A16 int4 weight-only linear layer (libw4a16.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels (device entry points) or its C++ host routines (quantise / pack).
+PyTorch supplies device memory and the current HIP stream.  The C entry points
+are exposed under their own names (``w4a16_gemv`` ...) on ``lib``; the
+functions below wrap them for torch tensors.
+
+The library must have been built (``python -m w4a16_int4_weight_linear_amd.build``
+or ``__graft_entry__.build()``); importing without it raises ImportError, and
+there is no fallback path of any kind.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -m w4a16_int4_weight_linear_amd.build)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+# The entry points of include/w4a16.h with their C signatures.
+SIGNATURES = {
+    "w4a16_abi_version": (ctypes.c_int, []),
+    "w4a16_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "w4a16_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "w4a16_pack": (ctypes.c_int, [_vp, _i64, _i64, _vp]),
+    "w4a16_unpack": (ctypes.c_int, [_vp, _i64, _i64, _vp]),
+    "w4a16_gemv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
+    "w4a16_gemv_max_k": (_i64, [_i64]),
+    "w4a16_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "w4a16_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "w4a16_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
+}
+
+for _name, (_res, _args) in SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+    globals()[_name] = _fn
+
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_RANGE = range(8)
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib.w4a16_status_str(status).decode()}")
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise W4A16Error(status, what)
+
+
+# ---------------------------------------------------------------------------
+# Host routines (numpy in, numpy out).
+# ---------------------------------------------------------------------------
+def quantize(w: np.ndarray, group: int):
+    """fp32 w [n, k] -> (packed uint32 [n, k/8], scales fp16 [n, k/group])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    packed = np.empty((n, k // 8), dtype=np.uint32)
+    scales = np.empty((n, k // group if group else 0), dtype=np.float16)
+    _check(lib.w4a16_quantize(w.ctypes.data, n, k, group, packed.ctypes.data, scales.ctypes.data), "quantize")
+    return packed, scales
+
+
+def pack(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    n, k = q.shape
+    out = np.empty((n, k // 8), dtype=np.uint32)
+    _check(lib.w4a16_pack(q.ctypes.data, n, k, out.ctypes.data), "pack")
+    return out
+
+
+def unpack(packed: np.ndarray, k: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    n = packed.shape[0]
+    out = np.empty((n, k), dtype=np.int8)
+    _check(lib.w4a16_unpack(packed.ctypes.data, n, k, out.ctypes.data), "unpack")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Device routines (torch tensors on the current HIP device).
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _dev_packed(packed):
+    """uint32 words travel as torch.int32 (same bits)."""
+    torch = _torch()
+    if isinstance(packed, np.ndarray):
+        packed = torch.from_numpy(np.ascontiguousarray(packed).view(np.int32))
+    return packed
+
+
+def gemv(x, packed, scales, group: int, out=None, stream=None):
+    """y [m, n] fp16 = x [m, k] . deq(packed, scales)^T, 1 <= m <= 4."""
+    torch = _torch()
+    m, k = x.shape
+    n = packed.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _check(lib.w4a16_gemv(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k, group, _stream(stream)),
+           "w4a16_gemv")
+    return out
+
+
+def gemm_workspace(m: int, n: int, k: int, group: int, device=None):
+    """A zero-filled workspace tensor of the size w4a16_gemm needs (None if none)."""
+    torch = _torch()
+    nbytes = lib.w4a16_gemm_workspace_bytes(m, n, k, group)
+    if nbytes == 0:
+        return None
+    return torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device=device or "cuda")
+
+
+def gemm(x, packed, scales, group: int, out=None, workspace=None, stream=None):
+    """y [m, n] fp16 = x [m, k] . deq(packed, scales)^T for any m (fp16 MFMA, fp32 accumulate)."""
+    torch = _torch()
+    m, k = x.shape
+    n = packed.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = gemm_workspace(m, n, k, group, x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.w4a16_gemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k, group, _ptr(workspace),
+                          ws_bytes, _stream(stream)), "w4a16_gemm")
+    return out
+
+
+def grouped_gemm(x, packed, scales, offsets, group: int, out=None, stream=None):
+    """MoE grouped product: rows offsets[e]..offsets[e+1] of x use expert e's weights."""
+    torch = _torch()
+    rows, k = x.shape
+    experts, n = packed.shape[0], packed.shape[1]
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.float16, device=x.device)
+    _check(lib.w4a16_grouped_gemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(offsets), _ptr(out), experts, rows,
+                                  n, k, group, _stream(stream)), "w4a16_grouped_gemm")
+    return out
+
+
+__all__ = ["lib", "LIB_PATH", "SIGNATURES", "W4A16Error", "quantize", "pack", "unpack", "gemv", "gemm",
+           "gemm_workspace", "grouped_gemm"] + list(SIGNATURES)

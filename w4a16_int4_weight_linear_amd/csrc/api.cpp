@@ -1,0 +1,166 @@
+// api.cpp -- the C ABI of include/w4a16.h: argument validation, per-device
+// facts, and dispatch to the gfx950 kernels.
+//
+// Every check runs on the host before anything is launched, in a fixed order
+// (group, shape, null, alignment, size limits, device), so a CPU-only process
+// can exercise every validation error without touching a GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/w4a16.h"
+#include "kernels.hpp"
+
+namespace w4a16 {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+hipError_t g_dev_err[kMaxDevices];
+}  // namespace
+
+hipError_t current_device_info(DeviceInfo* out) {
+  int d = 0;
+  hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) return e;
+  if (d < 0 || d >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_dev_once[d], [d] {
+    DeviceInfo info;
+    info.device = d;
+    int cu = 0, lds = 0;
+    hipError_t err = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, d);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, d);
+    info.num_cu = cu;
+    info.max_lds = (size_t)lds;
+    g_dev[d] = info;
+    g_dev_err[d] = err;
+  });
+  if (g_dev_err[d] != hipSuccess) return g_dev_err[d];
+  *out = g_dev[d];
+  return hipSuccess;
+}
+
+}  // namespace w4a16
+
+namespace {
+
+using w4a16::DeviceInfo;
+
+bool valid_group(int32_t g) { return g == 32 || g == 128; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Packed weights and scales are addressed with 32-bit buffer offsets.
+constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int common_dense_checks(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
+                        int64_t m, int64_t n, int64_t k, int32_t group) {
+  if (!valid_group(group)) return W4A16_ERR_GROUP;
+  if (m < 0 || n < 0 || k < 0 || k % group) return W4A16_ERR_SHAPE;
+  if (m > kMaxDim || n > kMaxDim || k > kMaxDim) return W4A16_ERR_SHAPE;
+  if (m == 0 || n == 0) return -1;  // no-op
+  if (!y) return W4A16_ERR_NULL;
+  if (k > 0 && (!x || !packed || !scales)) return W4A16_ERR_NULL;
+  if (!aligned(y, 16) || (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2))))
+    return W4A16_ERR_ALIGN;
+  if (n * (k / 2) >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (m * k >= kMaxBufferBytes || m * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_status_str(int status) {
+  switch (status) {
+    case W4A16_OK: return "W4A16_OK";
+    case W4A16_ERR_NULL: return "W4A16_ERR_NULL: a required pointer is NULL";
+    case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE: invalid or unsupported sizes";
+    case W4A16_ERR_GROUP: return "W4A16_ERR_GROUP: group size must be 32 or 128";
+    case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN: pointer misaligned";
+    case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: workspace missing or too small";
+    case W4A16_ERR_HIP: return "W4A16_ERR_HIP: HIP runtime error";
+    case W4A16_ERR_RANGE: return "W4A16_ERR_RANGE: value out of range";
+    default: return "W4A16: unknown status";
+  }
+}
+
+int64_t w4a16_gemv_max_k(int64_t m) {
+  if (m < 1 || m > 4) return 0;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return 0;
+  // LDS use is linear in k; find the largest multiple of 32 that fits.
+  const size_t per32 = w4a16::gemv_lds_bytes(m, 32);
+  return per32 ? (int64_t)(dev.max_lds / per32) * 32 : 0;
+}
+
+int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+               int64_t n, int64_t k, int32_t group, void* stream) {
+  if (valid_group(group) && m > 4) return W4A16_ERR_SHAPE;
+  int c = common_dense_checks(x, packed, scales, y, m, n, k, group);
+  if (c < 0) return W4A16_OK;
+  if (c != W4A16_OK) return c;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
+  if (w4a16::gemv_lds_bytes(m, k) > dev.max_lds) return W4A16_ERR_SHAPE;
+  return status_of(w4a16::launch_gemv(x, packed, scales, y, (int)m, (int)n, (int)k, group, dev, st));
+}
+
+size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group) {
+  if (!valid_group(group) || m <= 0 || n <= 0 || k <= 0 || k % group) return 0;
+  if (m > kMaxDim || n > kMaxDim || k > kMaxDim) return 0;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return 0;
+  return w4a16::gemm_workspace_bytes(m, n, k, group, dev);
+}
+
+int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+               int64_t n, int64_t k, int32_t group, void* workspace, size_t workspace_bytes, void* stream) {
+  int c = common_dense_checks(x, packed, scales, y, m, n, k, group);
+  if (c < 0) return W4A16_OK;
+  if (c != W4A16_OK) return c;
+  if (workspace && !aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
+  const size_t need = w4a16::gemm_workspace_bytes(m, n, k, group, dev);
+  if (need && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
+  return status_of(w4a16::launch_gemm(x, packed, scales, y, (int)m, (int)n, (int)k, group,
+                                      need ? workspace : nullptr, dev, st));
+}
+
+int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
+                       uint16_t* y, int32_t num_experts, int64_t rows, int64_t n, int64_t k, int32_t group,
+                       void* stream) {
+  if (!valid_group(group)) return W4A16_ERR_GROUP;
+  if (num_experts < 0 || rows < 0 || n < 0 || k < 0 || k % group) return W4A16_ERR_SHAPE;
+  if (rows > kMaxDim || n > kMaxDim || k > kMaxDim) return W4A16_ERR_SHAPE;
+  if (rows == 0 || n == 0) return W4A16_OK;
+  if (num_experts == 0) return W4A16_ERR_SHAPE;  // rows exist but no expert owns them
+  if (!y || !offsets) return W4A16_ERR_NULL;
+  if (k > 0 && (!x || !packed || !scales)) return W4A16_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(offsets, 4) ||
+      (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2))))
+    return W4A16_ERR_ALIGN;
+  if ((int64_t)num_experts * n * (k / 2) >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (rows * k >= kMaxBufferBytes || rows * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(rows * n), st));
+  return status_of(w4a16::launch_grouped_gemm(x, packed, scales, offsets, y, num_experts, (int)rows, (int)n,
+                                              (int)k, group, dev, st));
+}
+
+}  // extern "C"

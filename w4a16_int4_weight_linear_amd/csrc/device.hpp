@@ -1,0 +1,70 @@
+// device.hpp -- small gfx950 device helpers shared by the W4A16 kernels.
+//
+// Nothing here is specific to one kernel: buffer-resource loads (out-of-range
+// offsets return zero and touch no memory, which is how tails and padding are
+// masked without branches), the fp16 pair dot product, and DPP reductions
+// across a 64-wide wavefront.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format).
+constexpr int kRawBufferFlags = 0x00020000;
+// Cache policy bit for data streamed exactly once (non-temporal).
+constexpr int kStream = 2;
+
+// An offset that lies outside every buffer: loads from it return 0.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
+
+// acc + a.lo * b.lo + a.hi * b.hi, products of fp16 pairs accumulated in fp32.
+__device__ inline float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+
+__device__ inline float half_bits_to_float(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ inline uint16_t float_to_half_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);  // round to nearest even
+}
+
+template <int CTRL>
+__device__ inline float dpp_add(float v) {
+  int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+// Sum over all 64 lanes; every lane receives the total.  Within each 16-lane
+// DPP row: swap neighbours, swap pairs, then rotate by 4 and by 8; the four
+// row sums are then combined through scalar reads of lanes 0, 16, 32, 48.
+__device__ inline float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x124>(v);  // row_ror:4
+  v = dpp_add<0x128>(v);  // row_ror:8
+  int b = __builtin_bit_cast(int, v);
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ inline int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+}  // namespace w4a16

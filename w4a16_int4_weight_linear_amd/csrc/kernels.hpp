@@ -1,0 +1,42 @@
+// kernels.hpp -- host-side launchers of the gfx950 W4A16 kernels.
+//
+// The launchers take already-validated arguments (api.cpp checks every
+// argument before calling them) and return the HIP error of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+struct DeviceInfo {
+  int device = 0;
+  int num_cu = 0;
+  size_t max_lds = 0;  // bytes of LDS one workgroup may allocate
+};
+
+// Cached per-device facts of the current device.
+hipError_t current_device_info(DeviceInfo* out);
+
+// ---- decode GEMV (gemv.hip) ----
+// Bytes of LDS the GEMV needs for m activation rows of length k.
+size_t gemv_lds_bytes(int64_t m, int64_t k);
+hipError_t launch_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
+                       int m, int n, int k, int group, const DeviceInfo& dev, hipStream_t stream);
+
+// ---- prefill GEMM (gemm.hip) ----
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int group, const DeviceInfo& dev);
+hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
+                       int m, int n, int k, int group, void* workspace, const DeviceInfo& dev,
+                       hipStream_t stream);
+
+// ---- MoE grouped GEMM (grouped_gemm.hip) ----
+hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                               const int32_t* offsets, uint16_t* y, int experts, int rows, int n, int k,
+                               int group, const DeviceInfo& dev, hipStream_t stream);
+
+// ---- y = 0 (the empty sum, k == 0) ----
+hipError_t launch_zero_fill(uint16_t* y, size_t count, hipStream_t stream);
+
+}  // namespace w4a16
