@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 W4A16 int4 weight-only linear layer.
+
+One step = one decode token through the dense 27B-like FFN's two weight
+streams at M = 1: the up projection (K=5120 -> N=17408) and the down
+projection (K=17408 -> N=5120), both group 128, run back to back as two
+w4a16_gemv launches.  ``value`` is that step's algorithmic HBM traffic
+(packed weights + scales + activations + outputs, each moved once) over its
+measured time, in GB/s.  The same JSON line also reports the other parts of the
+hot path on their own workloads: batched decode (M = 4), prefill GEMM (M = 512
+and M = 4096, TFLOP/s) and the MoE grouped GEMM (256 experts, GB/s).
+
+Inputs are seeded synthetic draws (``synth``) of the workload shapes; every
+weight read in the timed region comes from a rotating pool of distinct copies
+totalling at least 1 GiB, so no call finds its weights in the 256 MB
+last-level cache.  Inputs are resident in HBM before timing starts.
+
+``--gpus N`` with N > 1 is refused: this layer is measured on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
+POOL_BYTES = 1 << 30           # rotating weight pool per workload
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--components", default="decode,np4,prefill,moe",
+                    help="comma list of parts to measure (decode is the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic sizes.
+# ---------------------------------------------------------------------------
+def dense_bytes(m, n, k, group):
+    return n * k // 2 + n * (k // group) * 2 + m * k * 2 + m * n * 2
+
+
+def dense_flops(m, n, k):
+    return 2 * m * n * k
+
+
+# ---------------------------------------------------------------------------
+# Device setup helpers.
+# ---------------------------------------------------------------------------
+def make_pool(torch, packed_np, scales_np, min_bytes=POOL_BYTES):
+    """Distinct device copies of (packed, scales), together >= min_bytes."""
+    p = torch.from_numpy(np.ascontiguousarray(packed_np).view(np.int32)).to("cuda")
+    s = torch.from_numpy(np.ascontiguousarray(scales_np)).to("cuda")
+    per = p.numel() * 4 + s.numel() * 2
+    copies = max(2, -(-min_bytes // per))
+    pool = [(p, s)] + [(p.clone(), s.clone()) for _ in range(copies - 1)]
+    return pool
+
+
+def timed(torch, fn, steps, warmup):
+    """Mean ms per call of fn(i) over `steps` calls, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def per_launch(torch, fn, steps):
+    """Mean ms of each launch of fn(i), bracketed by its own pair of events."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(t.mean()), float(np.median(t))
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "w4a16_int4_weight_linear_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file, kernel_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_file}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# Components.
+# ---------------------------------------------------------------------------
+def decode_component(torch, w4, synth, args):
+    up = synth.DENSE_CASES["gemv_up_1x5120x17408_g128"]
+    down = synth.DENSE_CASES["gemv_down_1x17408x5120_g128"]
+    wu, xu = synth.dense_inputs(up)
+    wd, xd = synth.dense_inputs(down)
+    pu, su = w4.quantize(wu, 128)
+    pd, sd = w4.quantize(wd, 128)
+    pool_u = make_pool(torch, pu, su, POOL_BYTES // 2)
+    pool_d = make_pool(torch, pd, sd, POOL_BYTES // 2)
+    xu_t = torch.from_numpy(xu).to("cuda")
+    xd_t = torch.from_numpy(xd).to("cuda")
+    yu = torch.empty((1, up.n), dtype=torch.float16, device="cuda")
+    yd = torch.empty((1, down.n), dtype=torch.float16, device="cuda")
+
+    def step(i):
+        p, s = pool_u[i % len(pool_u)]
+        w4.gemv(xu_t, p, s, 128, out=yu)
+        p, s = pool_d[i % len(pool_d)]
+        w4.gemv(xd_t, p, s, 128, out=yd)
+
+    ms = timed(torch, step, args.steps, args.warmup)
+    step_bytes = dense_bytes(1, up.n, up.k, 128) + dense_bytes(1, down.n, down.k, 128)
+
+    def one_up(i):
+        p, s = pool_u[i % len(pool_u)]
+        w4.gemv(xu_t, p, s, 128, out=yu)
+
+    def one_down(i):
+        p, s = pool_d[i % len(pool_d)]
+        w4.gemv(xd_t, p, s, 128, out=yd)
+
+    up_mean, up_med = per_launch(torch, one_up, args.steps)
+    dn_mean, dn_med = per_launch(torch, one_down, args.steps)
+    launch_ms = (up_mean + dn_mean) / 2
+    launch_bytes = dense_bytes(1, up.n, up.k, 128)   # the two launches move equal bytes
+    return {
+        "ms_per_step": ms,
+        "step_bytes": step_bytes,
+        "gbs": step_bytes / (ms * 1e-3) / 1e9,
+        "kernel": {"name": "gemv_kernel<1>", "launch_ms_up": up_mean, "launch_ms_down": dn_mean,
+                   "launch_ms_median_up": up_med, "launch_ms_median_down": dn_med,
+                   "launch_ms": launch_ms, "bytes_per_launch": launch_bytes,
+                   "gbs": launch_bytes / (launch_ms * 1e-3) / 1e9},
+        "inputs": (wu, xu, wd, xd),
+        "quantized": ((pu, su), (pd, sd)),
+    }
+
+
+def np4_component(torch, w4, synth, args):
+    out = {}
+    for name in ("gemv_np4_4x5120x5120_g128", "gemv_np4_4x5120x17408_g128"):
+        c = synth.DENSE_CASES[name]
+        w, x = synth.dense_inputs(c)
+        p, s = w4.quantize(w, c.group)
+        pool = make_pool(torch, p, s)
+        xt = torch.from_numpy(x).to("cuda")
+        y = torch.empty((c.m, c.n), dtype=torch.float16, device="cuda")
+
+        def one(i):
+            pp, ss = pool[i % len(pool)]
+            w4.gemv(xt, pp, ss, c.group, out=y)
+
+        mean, med = per_launch(torch, one, args.steps)
+        b = dense_bytes(c.m, c.n, c.k, c.group)
+        out[name] = {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
+                     "gbs": b / (mean * 1e-3) / 1e9, "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
+def prefill_component(torch, w4, synth, args):
+    out = {}
+    c0 = synth.DENSE_CASES["gemm_4096x5120x17408_g128"]
+    w, x_all = synth.dense_inputs(c0)
+    p, s = w4.quantize(w, 128)
+    pool = make_pool(torch, p, s)
+    for name in ("gemm_512x5120x17408_g128", "gemm_4096x5120x17408_g128"):
+        c = synth.DENSE_CASES[name]
+        xt = torch.from_numpy(x_all[: c.m]).to("cuda")
+        y = torch.empty((c.m, c.n), dtype=torch.float16, device="cuda")
+        ws = w4.gemm_workspace(c.m, c.n, c.k, c.group)
+
+        def one(i):
+            pp, ss = pool[i % len(pool)]
+            w4.gemm(xt, pp, ss, c.group, out=y, workspace=ws)
+
+        steps = args.steps if c.m <= 512 else max(20, args.steps // 4)
+        for i in range(min(args.warmup, 10)):
+            one(i)
+        mean, med = per_launch(torch, one, steps)
+        fl = dense_flops(c.m, c.n, c.k)
+        out[name] = {"launch_ms": mean, "launch_ms_median": med, "flops": fl,
+                     "tflops": fl / (mean * 1e-3) / 1e12,
+                     "mfma_frac": fl / (mean * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+    return out
+
+
+def moe_component(torch, w4, synth, args):
+    c = synth.MOE_CASES["moe_256e_512x2048_g32_top8"]
+    ws, x, r = synth.moe_inputs(c)
+    packed = np.empty((c.experts, c.n, c.k // 8), np.uint32)
+    scales = np.empty((c.experts, c.n, c.k // c.group), np.float16)
+    for e, w in enumerate(ws):
+        packed[e], scales[e] = w4.quantize(w, c.group)
+    del ws
+    pool = make_pool(torch, packed, scales)
+    xs = torch.from_numpy(x[r.pair_token]).to("cuda")
+    offs = torch.from_numpy(r.offsets).to("cuda")
+    rows = len(r.pair_token)
+    y = torch.empty((rows, c.n), dtype=torch.float16, device="cuda")
+
+    def one(i):
+        pp, ss = pool[i % len(pool)]
+        w4.grouped_gemm(xs, pp, ss, offs, c.group, out=y)
+
+    mean, med = per_launch(torch, one, args.steps)
+    b = c.experts * c.n * c.k // 2 + c.experts * c.n * (c.k // c.group) * 2 + rows * c.k * 2 + rows * c.n * 2 \
+        + (c.experts + 1) * 4
+    fl = dense_flops(rows, c.n, c.k)
+    return {"launch_ms": mean, "launch_ms_median": med, "bytes": b, "gbs": b / (mean * 1e-3) / 1e9,
+            "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, "tflops": fl / (mean * 1e-3) / 1e12}
+
+
+def cpu_baseline(decode):
+    """The fp64 oracle on the host, over one decode step (up + down), timed."""
+    import oracle
+    wu, xu, wd, xd = decode["inputs"]
+    (pu, su), (pd, sd) = decode["quantized"]
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.linear(xu, pu, su, 128)
+        oracle.linear(xd, pd, sd, 128)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 5:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": decode["step_bytes"] / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{reps} decode step(s) (up 1x5120->17408 + down 1x17408->5120, g128): fp64 dequantise "
+                      f"+ numpy matmul, {dt:.2f} s per step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1",
+                          "reason": "the W4A16 layer is built and measured on a single MI355X"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    import synth
+    import w4a16_int4_weight_linear_amd as w4
+
+    comps = [c for c in args.components.split(",") if c]
+    res = {}
+    decode = decode_component(torch, w4, synth, args)
+    if "np4" in comps:
+        res["np4"] = np4_component(torch, w4, synth, args)
+    if "prefill" in comps:
+        res["prefill"] = prefill_component(torch, w4, synth, args)
+    if "moe" in comps:
+        res["moe"] = moe_component(torch, w4, synth, args)
+
+    k = decode["kernel"]
+    traffic = traffic_from_profile("gemv", source_hash("gemv.hip", "device.hpp"))
+    line = {
+        "metric": "W4A16 GEMV HBM GB/s (M=1) + GEMM TFLOP/s (M=512), % of MI355X roofline",
+        "value": round(decode["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(decode["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 activations x int4 weights, f32 accumulate",
+        "data": "synthetic (seeded Gaussian weights quantised int4 sym g128; fp16 N(0,1) activations)",
+        "config": {"workload": "decode GEMV M=1, 27B-like dense FFN: up K=5120->N=17408 + down K=17408->N=5120, g128",
+                   "m": 1, "group": 128, "rotating_weight_pool_bytes": POOL_BYTES},
+        "roofline": {"bound": "hbm", "achieved": round(k["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": k["name"], "launch_us": round(k["launch_ms"] * 1e3, 3),
+                     "bytes_per_launch": k["bytes_per_launch"]},
+        "hbm_frac_step": round(decode["gbs"] / HBM_PEAK_GBS, 4),
+    }
+    line.update({key: val for key, val in res.items()})
+    if "prefill" in res and "gemm_512x5120x17408_g128" in res["prefill"]:
+        g = res["prefill"]["gemm_512x5120x17408_g128"]
+        line["gemm_m512"] = {"tflops": round(g["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                             "frac": round(g["mfma_frac"], 4), "launch_us": round(g["launch_ms"] * 1e3, 2)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(decode)
+    print(json.dumps(line, default=float))
+
+
+if __name__ == "__main__":
+    main()

@@ -96,16 +96,19 @@ int w4a16_unpack(const uint32_t* packed, int64_t n, int64_t k, int8_t* q);
  * of the LLM170 CUDA/W4A16 page's benchmark tables): y = x . deq(W)^T.
  * All m rows share one pass over the packed weights.  x [m, k] and y [m, n]
  * fp16, packed [n, k/8], scales [n, k/group], all on the device.
- * The activations are staged in on-chip memory (LDS), which bounds k:
- * W4A16_ERR_SHAPE if k > w4a16_gemv_max_k(m) (w4a16_gemm takes any size).
+ * The activations and the scales of the rows in flight are staged in on-chip
+ * memory (LDS), which bounds k: every k <= w4a16_gemv_max_k(m, group) is
+ * accepted; larger k may be rejected with W4A16_ERR_SHAPE (w4a16_gemm takes
+ * any size).
  */
 int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
                void* stream);
 
-/* Largest k w4a16_gemv accepts for m rows on the current device (0 if m is
- * outside 1..4 or no device is usable). */
-int64_t w4a16_gemv_max_k(int64_t m);
+/* Largest k w4a16_gemv accepts for every n, for m rows and this group size on
+ * the current device (0 if m is outside 1..4, the group is invalid or no
+ * device is usable). */
+int64_t w4a16_gemv_max_k(int64_t m, int32_t group);
 
 /*
  * Bytes of device workspace w4a16_gemm needs for this problem on the current

@@ -151,7 +151,8 @@ def test_gemv_validation():
     # empty problems succeed without touching anything
     assert g(None, None, None, None, 0, 64, 128, 128, None) == w4.OK
     assert g(None, None, None, None, 1, 0, 128, 128, None) == w4.OK
-    assert w4.lib.w4a16_gemv_max_k(0) == 0 and w4.lib.w4a16_gemv_max_k(5) == 0
+    assert w4.lib.w4a16_gemv_max_k(0, 128) == 0 and w4.lib.w4a16_gemv_max_k(5, 128) == 0
+    assert w4.lib.w4a16_gemv_max_k(1, 64) == 0
 
 
 def test_gemm_validation():

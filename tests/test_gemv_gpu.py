@@ -111,7 +111,7 @@ def test_gemv_empty_k_gives_zero(w4):
 
 def test_gemv_max_k_is_usable(w4):
     for m in (1, 4):
-        kmax = w4.lib.w4a16_gemv_max_k(m)
+        kmax = w4.lib.w4a16_gemv_max_k(m, 128)
         assert kmax >= 17408, (m, kmax)
         k = (kmax // 128) * 128
         rng = np.random.default_rng(4000 + m)
@@ -120,6 +120,7 @@ def test_gemv_max_k_is_usable(w4):
         s = np.full((8, k // 128), 2.0 ** -8, np.float16)
         y = run_gemv(w4, x, w4.pack(q), s, 128)
         assert_bit_exact(y, oracle.linear(x, oracle.pack(q), s, 128), f"m={m} k={k}")
+        k2 = kmax + 4096
         with pytest.raises(w4.W4A16Error):
-            w4.gemv(dev(np.zeros((m, kmax + 128), np.float16)), dev(np.zeros((8, (kmax + 128) // 8), np.uint32)),
-                    dev(np.zeros((8, (kmax + 128) // 128), np.float16)), 128)
+            w4.gemv(dev(np.zeros((m, k2), np.float16)), dev(np.zeros((8, k2 // 8), np.uint32)),
+                    dev(np.zeros((8, k2 // 128), np.float16)), 128)

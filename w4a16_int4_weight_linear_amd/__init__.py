@@ -36,7 +36,7 @@ SIGNATURES = {
     "w4a16_pack": (ctypes.c_int, [_vp, _i64, _i64, _vp]),
     "w4a16_unpack": (ctypes.c_int, [_vp, _i64, _i64, _vp]),
     "w4a16_gemv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
-    "w4a16_gemv_max_k": (_i64, [_i64]),
+    "w4a16_gemv_max_k": (_i64, [_i64, _i32]),
     "w4a16_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "w4a16_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),

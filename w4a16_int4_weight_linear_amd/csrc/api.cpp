@@ -93,13 +93,11 @@ const char* w4a16_status_str(int status) {
   }
 }
 
-int64_t w4a16_gemv_max_k(int64_t m) {
-  if (m < 1 || m > 4) return 0;
+int64_t w4a16_gemv_max_k(int64_t m, int32_t group) {
+  if (m < 1 || m > 4 || !valid_group(group)) return 0;
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return 0;
-  // LDS use is linear in k; find the largest multiple of 32 that fits.
-  const size_t per32 = w4a16::gemv_lds_bytes(m, 32);
-  return per32 ? (int64_t)(dev.max_lds / per32) * 32 : 0;
+  return w4a16::gemv_max_k((int)m, group, dev);
 }
 
 int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
@@ -112,8 +110,9 @@ int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
-  if (w4a16::gemv_lds_bytes(m, k) > dev.max_lds) return W4A16_ERR_SHAPE;
-  return status_of(w4a16::launch_gemv(x, packed, scales, y, (int)m, (int)n, (int)k, group, dev, st));
+  const w4a16::GemvPlan plan = w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev);
+  if (!plan.ok) return W4A16_ERR_SHAPE;
+  return status_of(w4a16::launch_gemv(x, packed, scales, y, (int)m, (int)n, (int)k, group, plan, dev, st));
 }
 
 size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group) {

@@ -30,6 +30,24 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
 }
 
+// 16 bytes at byte offset `off` of a buffer of `bytes` bytes.  A load that
+// reaches past the end is out of range as a whole and would return zero, so the
+// partial last chunk of a buffer is assembled from 2-byte loads (each either
+// fully inside or fully outside); bytes past the end read as zero.
+__device__ inline u32x4 load16_tail(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t bytes) {
+  if (off >= bytes || off + 16u <= bytes) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4u * i, 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4u * i + 2u, 0, 0);
+    w[i] = (lo & 0xFFFFu) | (hi << 16);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // acc + a.lo * b.lo + a.hi * b.hi, products of fp16 pairs accumulated in fp32.
 __device__ inline float dot2(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);

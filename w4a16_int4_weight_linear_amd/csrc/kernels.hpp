@@ -20,10 +20,18 @@ struct DeviceInfo {
 hipError_t current_device_info(DeviceInfo* out);
 
 // ---- decode GEMV (gemv.hip) ----
-// Bytes of LDS the GEMV needs for m activation rows of length k.
-size_t gemv_lds_bytes(int64_t m, int64_t k);
+struct GemvPlan {
+  int waves_total = 0, rows_base = 0, rows_extra = 0;
+  size_t lds = 0;     // bytes of LDS per workgroup
+  bool ok = false;    // false: the activations and scales do not fit in LDS
+};
+// Launch plan (work split and LDS size) for an m x k by n x k problem.
+GemvPlan gemv_plan(int m, int n, int k, int group, const DeviceInfo& dev);
+// Largest k (a multiple of group) that has a feasible plan for every n.
+int64_t gemv_max_k(int m, int group, const DeviceInfo& dev);
 hipError_t launch_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
-                       int m, int n, int k, int group, const DeviceInfo& dev, hipStream_t stream);
+                       int m, int n, int k, int group, const GemvPlan& plan, const DeviceInfo& dev,
+                       hipStream_t stream);
 
 // ---- prefill GEMM (gemm.hip) ----
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int group, const DeviceInfo& dev);
