@@ -1,0 +1,91 @@
+"""Prefill GEMM parity against the fp64 oracle, through the C ABI.
+
+Integer activations, codes and power-of-two scales make every MFMA product and
+partial sum exact, so those outputs must equal the oracle's fp16 rounding bit
+for bit; Gaussian inputs must meet the tolerances of oracle.check.  The
+full-size prefill workloads run in the same launch configuration the
+benchmark times and are checked on sampled full rows.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_bit_exact, assert_close, dev, gaussian_sides, host, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w4():
+    torch_mod()
+    import w4a16_int4_weight_linear_amd as w4
+    return w4
+
+
+def run_gemm(w4, x, packed, scales, group):
+    y = w4.gemm(dev(x), dev(packed), dev(scales), group)
+    torch_mod().cuda.synchronize()
+    return host(y)
+
+
+# (m, n, k, group): one row, ragged M/N tiles, a K tail of 32 (K % 64 != 0),
+# several K steps, both group sizes.
+EXACT_SHAPES = [(1, 64, 128, 128), (7, 300, 256, 32), (128, 256, 512, 128), (130, 260, 1024, 32),
+                (257, 513, 5120, 128), (64, 100, 96, 32), (300, 1000, 2080, 32), (512, 17408 // 8, 640, 128)]
+
+
+@pytest.mark.parametrize("m,n,k,group", EXACT_SHAPES)
+def test_gemm_exact_integer_family(w4, m, n, k, group):
+    rng = np.random.default_rng(5000 + m + n + k + group)
+    x = synth.integer_activations(rng, m, k)
+    q = synth.integer_codes(rng, n, k)
+    s = synth.power_of_two_scales(rng, n, k // group, lo=-6, hi=-3)
+    y = run_gemm(w4, x, w4.pack(q), s, group)
+    assert_bit_exact(y, oracle.linear(x, oracle.pack(q), s, group), f"m={m} n={n} k={k} g={group}")
+
+
+@pytest.mark.parametrize("m,n,k,group", [(512, 1024, 2048, 128), (333, 777, 1280, 32), (4, 4096, 5120, 128)])
+def test_gemm_gaussian(w4, m, n, k, group):
+    rng = np.random.default_rng(6000 + m)
+    w = synth.weights(rng, n, k)
+    x = synth.activations(rng, m, k)
+    (p, s), (p_ref, s_ref) = gaussian_sides(w4, w, group)
+    y = run_gemm(w4, x, p, s, group)
+    assert_close(y, oracle.linear(x, p_ref, s_ref, group), f"m={m} n={n} k={k} g={group}")
+
+
+@pytest.mark.parametrize("name", ["gemm_512x5120x17408_g128", "gemm_4096x5120x17408_g128"])
+def test_gemm_workload_full_size_sampled(w4, name):
+    """The prefill workloads at full size; 48 sampled full output rows vs the oracle."""
+    case = synth.DENSE_CASES[name]
+    w, x = synth.dense_inputs(case)
+    (p, s), (p_ref, s_ref) = gaussian_sides(w4, w, case.group)
+    y = run_gemm(w4, x, p, s, case.group)
+    rows = np.sort(np.random.default_rng(7).choice(case.m, 48, replace=False))
+    rep = assert_close(y[rows], oracle.linear_rows(x, p_ref, s_ref, case.group, rows), name)
+    assert np.isfinite(y).all()
+    print(f"{name}: {rep.message}")
+
+
+def test_gemm_matches_gemv_for_small_m(w4):
+    """Two independent kernels on the same problem agree within the oracle's bars."""
+    rng = np.random.default_rng(6100)
+    w = synth.weights(rng, 2000, 3072)
+    x = synth.activations(rng, 4, 3072)
+    p, s = w4.quantize(w, 128)
+    yg = run_gemm(w4, x, p, s, 128)
+    yv = host(w4.gemv(dev(x), dev(p), dev(s), 128))
+    assert_close(yg, yv.astype(np.float64), "gemm vs gemv")
+
+
+def test_gemm_deterministic(w4):
+    rng = np.random.default_rng(6200)
+    w = synth.weights(rng, 1500, 2048)
+    x = synth.activations(rng, 300, 2048)
+    p, s = w4.quantize(w, 32)
+    xd, pd, sd = dev(x), dev(p), dev(s)
+    y1 = host(w4.gemm(xd, pd, sd, 32))
+    y2 = host(w4.gemm(xd, pd, sd, 32))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
