@@ -86,16 +86,22 @@ def timed(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
-def per_launch(torch, fn, steps):
-    """Mean ms of each launch of fn(i), bracketed by its own pair of events."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record()
-        fn(i)
-        evs[i][1].record()
+def per_launch(torch, fn, steps, batches=5):
+    """Mean ms per launch of fn(i): `batches` runs of `steps` back-to-back launches,
+    each run bracketed by one pair of events on the launch stream.  Returns
+    (mean, median over the runs)."""
+    fn(0)
     torch.cuda.synchronize()
-    t = np.array([a.elapsed_time(b) for a, b in evs])
-    return float(t.mean()), float(np.median(t))
+    per = []
+    for b in range(batches):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            fn(b * steps + i)
+        stop.record()
+        torch.cuda.synchronize()
+        per.append(start.elapsed_time(stop) / steps)
+    return float(np.mean(per)), float(np.median(per))
 
 
 def source_hash(*names):
@@ -206,10 +212,10 @@ def prefill_component(torch, w4, synth, args):
             pp, ss = pool[i % len(pool)]
             w4.gemm(xt, pp, ss, c.group, out=y, workspace=ws)
 
-        steps = args.steps if c.m <= 512 else max(20, args.steps // 4)
+        steps = args.steps if c.m <= 512 else max(10, args.steps // 8)
         for i in range(min(args.warmup, 10)):
             one(i)
-        mean, med = per_launch(torch, one, steps)
+        mean, med = per_launch(torch, one, steps, batches=3)
         fl = dense_flops(c.m, c.n, c.k)
         out[name] = {"launch_ms": mean, "launch_ms_median": med, "flops": fl,
                      "tflops": fl / (mean * 1e-3) / 1e12,
