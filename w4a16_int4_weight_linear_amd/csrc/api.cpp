@@ -52,7 +52,8 @@ using w4a16::DeviceInfo;
 bool valid_group(int32_t g) { return g == 32 || g == 128; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Packed weights and scales are addressed with 32-bit buffer offsets.
+// Activations, packed weights and scales are addressed with 32-bit buffer
+// offsets below 2^31 (an offset of 2^31 marks an out-of-range load).
 constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
@@ -67,7 +68,7 @@ int common_dense_checks(const uint16_t* x, const uint32_t* packed, const uint16_
   if (!aligned(y, 16) || (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2))))
     return W4A16_ERR_ALIGN;
   if (n * (k / 2) >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
-  if (m * k >= kMaxBufferBytes || m * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (2 * m * k >= kMaxBufferBytes || 2 * m * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
   return W4A16_OK;
 }
 
@@ -153,7 +154,7 @@ int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
       (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2))))
     return W4A16_ERR_ALIGN;
   if ((int64_t)num_experts * n * (k / 2) >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
-  if (rows * k >= kMaxBufferBytes || rows * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (2 * rows * k >= kMaxBufferBytes || 2 * rows * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -5,28 +5,41 @@
 // pp1024, pp4096 columns).  Here the layer is a dense contraction, so it runs
 // on the matrix cores: v_mfma_f32_32x32x16_f16, fp16 inputs, fp32 accumulation.
 //
-// * Tiles: 128 x 256 output tiles, K steps of 64.  A 256-thread workgroup
-//   runs four wavefronts of 128 x 64 (4 x 2 MFMA blocks of 32 x 32, 128 fp32
-//   accumulators per lane, held in the accumulation registers); one
-//   persistent workgroup per CU.
-// * A software pipeline hides memory latency: the loads of K step k + 3 are
-//   in flight while step k computes.  Activations (the MFMA A operand) come
-//   into a ring of registers, are written to a double-buffered LDS tile
-//   (128 x 64 per step) one step before use, with an XOR swizzle of the
-//   16-byte chunks so the MFMA operand reads are free of bank conflicts.
-//   Weights (the B operand) never touch LDS: each lane loads one 16-byte
-//   packed chunk per 32-column block and K step into a ring of registers and
-//   dequantises it in natural k order (mfma_operands.hpp).
-// * Work split (stream-K, per XCD): the tiles are dealt to the 8 XCDs in
-//   contiguous, column-band-major ranges (each packed weight is read from HBM
-//   by one XCD only); inside an XCD the (tile, K step) iterations are split
-//   evenly over its persistent workgroups, so a tile may be shared by two or
-//   more workgroups.  Every workgroup walks its range from the end, and the
-//   workgroup holding a tile's last K step finishes it: the others store fp32
-//   partial tiles in the workspace and raise a flag; the finisher waits for
-//   the flags of lower-numbered workgroups only (dispatched earlier), adds the
-//   partials in a fixed order (deterministic) and writes fp16.  It clears the
-//   flags it consumed, so the workspace stays ready for the next call.
+// * Tiles: 128 x 256 outputs, K steps of 128.  One persistent 256-thread
+//   workgroup per CU; each of its four wavefronts (one per SIMD) owns a
+//   128 x 64 slab (4 x 2 MFMA blocks of 32 x 32, 128 fp32 accumulators per
+//   lane, kept in the accumulation registers).
+// * The activation tile (128 x 128 fp16) and the packed weight tile (256 rows
+//   x 64 bytes) of a K step go through a three-stage LDS ring (144 KB): they
+//   are loaded straight from global memory into LDS (buffer loads with the
+//   LDS bit: no registers, no LDS write instructions), 16 lanes per
+//   activation row and 4 per weight row, so every 64-byte L2 request is used
+//   whole.  Step r + 2 is loaded while step r computes.  The LDS layouts are
+//   XOR-swizzled, so every operand read is free of bank conflicts.
+// * Scales come in windows of 8 consecutive groups per weight row: one
+//   16-byte global-to-LDS load per row per window into a double-buffered
+//   LDS area (8 KB), issued in the first step of the previous window.
+//   Loading the one 2-byte scale of a row per step instead would cost one
+//   L2 request per row and step, about a third of all requests.  The load
+//   is issued in every step, so the step code has no branch: in the steps
+//   that need none it goes to a dummy LDS area with an out-of-range global
+//   offset (no memory access).  When the rows' scales are not 16-byte
+//   aligned (K / g not a multiple of 8), each stage carries its step's
+//   scales instead (2-byte loads, stored zero-extended to 4 bytes).
+// * Within a step a wavefront runs 8 MFMA sub-steps of 16 k.  The activation
+//   operands of sub-step s + 2 are read from LDS and the weights of sub-step
+//   s + 1 are dequantised in registers (mfma_operands.hpp) while the MFMAs of
+//   sub-step s run; both run across the end of a step, so after the one
+//   barrier per step the matrix cores restart at once.  Scheduling groups
+//   interleave each MFMA with a few VALU instructions and LDS or global
+//   accesses, and a scheduling fence after every sub-step keeps that
+//   pipeline order.
+// * Work split: whole tiles in data-parallel rounds, the 32 workgroups of an
+//   XCD on a 4 x 8 block of neighbouring tiles (shared operands stay in the
+//   XCD's L2); the tiles left over after the last full round are split
+//   along K (stream-K) over the XCD's workgroups, computed first, and reduced
+//   at the end by their contributors in a fixed order (deterministic).  The
+//   details are at gemm_plan.
 //
 // For integer activations, codes and power-of-two scales every product and
 // partial sum is exact, so such inputs give bit-exact results.
@@ -39,21 +52,42 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWGPerCU = 1;
-constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int BM = 128, BN = 256, BK = 128;
 constexpr int kWaveN = 64;                  // output columns per wave
 constexpr int kMB = BM / 32, kNB = kWaveN / 32;
-constexpr int kAhead = 3;                   // K steps between a load and its use
-constexpr int kUnroll = 6;                  // lcm(register ring 3, LDS double buffer 2)
-constexpr int kATile = BM * BK * 2;         // bytes per LDS A buffer (128 rows of 128 bytes, swizzled)
+constexpr int kSub = BK / 16;               // MFMA sub-steps per K step
+constexpr int kABytes = BM * BK * 2;        // activation tile: 128 rows of 256 bytes
+constexpr int kBBytes = BN * BK / 2;        // packed weight tile: 256 rows of 64 bytes
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kWinBytes = BN * 16;            // one scale window: 256 rows x 8 groups x 2 bytes
 constexpr int kXCD = 8;
-constexpr int kMinItersPerWG = 8;           // keep stream-K segments from getting tiny
 constexpr size_t kPartialBytes = (size_t)BM * BN * 4;
-constexpr uint32_t kSpinLimit = 1u << 24;   // flag polls before a finisher gives up
+constexpr uint32_t kSpinLimit = 1u << 24;   // flag polls before the fix-up gives up
+static_assert(3 * kStageBytes + 2 * kWinBytes + 1024 <= 160 * 1024, "LDS use exceeds 160 KB");
+static_assert(3 * (kStageBytes + BN * 4 * 4) <= 160 * 1024, "LDS use exceeds 160 KB");
 
+// Work split.  T output tiles of BM x BN, I K steps each, W persistent
+// workgroups (a multiple of the 8 XCDs; workgroup g runs on XCD g % 8).
+// * Data-parallel rounds: the first D = floor(T / W) * W tiles (in the
+//   grouped order of tile_coords) are computed whole, W at a time; in each
+//   round the 32 workgroups of an XCD take 32 consecutive tiles, a block of
+//   4 tile rows by 8 tile columns, so they share activation rows and weight
+//   columns in the XCD's L2 while they move through K in step.
+// * Stream-K remainder: the R = T - D leftover tiles are dealt to the XCDs in
+//   contiguous ranges, and an XCD's (tile, K step) iterations are split
+//   evenly over nsk of its workgroups (at least kMinSKSteps each), which
+//   compute them first and store fp32 partial tiles.  A workgroup's range is
+//   no longer than one tile, so it touches at most two tiles.
+// * Fix-up, last: the contributors of a stream-K tile each reduce one slice
+//   of it (all partials of the slice, in contributor order: deterministic)
+//   and write fp16.  By then every partial was published long before.
 struct GemmPlan {
   int tiles_m, tiles_n, tiles, iters;       // iters: K steps per tile
-  int wg_per_xcd, wgs;
+  int wgs, rounds, sk_tiles, nsk;           // nsk: stream-K workgroups per XCD
 };
+
+constexpr int kMinSKSteps = 2;
+constexpr int kGroupM = 4;                  // tile rows per group of the tile order
 
 GemmPlan gemm_plan(int m, int n, int k, const DeviceInfo& dev) {
   GemmPlan p;
@@ -61,33 +95,94 @@ GemmPlan gemm_plan(int m, int n, int k, const DeviceInfo& dev) {
   p.tiles_n = (n + BN - 1) / BN;
   p.tiles = p.tiles_m * p.tiles_n;
   p.iters = (k + BK - 1) / BK;
-  const long long total = (long long)p.tiles * p.iters;
   int per_xcd = (dev.num_cu * kWGPerCU) / kXCD;
-  const long long useful = (total / kXCD + kMinItersPerWG - 1) / kMinItersPerWG;
-  if (useful < per_xcd) per_xcd = (int)(useful < 1 ? 1 : useful);
-  p.wg_per_xcd = per_xcd < 1 ? 1 : per_xcd;
-  p.wgs = p.wg_per_xcd * kXCD;
+  if (per_xcd < 1) per_xcd = 1;
+  p.wgs = per_xcd * kXCD;
+  p.rounds = p.tiles / p.wgs;
+  p.sk_tiles = p.tiles - p.rounds * p.wgs;
+  // stream-K workgroups per XCD, from the busiest XCD's ceil(R / 8) tiles;
+  // at least one per tile, so no range is longer than a tile
+  const int cnt_max = (p.sk_tiles + kXCD - 1) / kXCD;
+  long long nsk = (long long)cnt_max * p.iters / kMinSKSteps;
+  if (nsk < cnt_max) nsk = cnt_max;
+  if (nsk > per_xcd) nsk = per_xcd;
+  p.nsk = p.sk_tiles ? (int)nsk : 0;
   return p;
 }
 
-// XOR swizzle of the 16-byte chunks of an LDS A row (128 bytes).  An operand
-// read has 16 lanes at a time reading one logical chunk of 16 consecutive
-// rows; with 64 four-byte banks two rows share a bank line, so the chunk is
-// moved by (row / 2) % 8: the 16 lanes land on 16 distinct bank quads.
-__device__ inline int swz(int row) { return (row >> 1) & 7; }
-
-__device__ inline int xcd_tile_begin(int xcd, int tiles) {
-  const int q = tiles / kXCD, r = tiles % kXCD;
+__device__ inline int xcd_begin(int xcd, int count) {
+  const int q = count / kXCD, r = count % kXCD;
   return xcd * q + (xcd < r ? xcd : r);
 }
 
+// Tile order: groups of kGroupM tile rows; inside a group, column by column.
+__device__ inline void tile_coords(int tau, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int grp = tau / per_group;
+  const int first_m = grp * kGroupM;
+  const int gsize = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int r = tau - grp * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+#define W4A16_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Barrier that publishes LDS: this thread's LDS reads and global-to-LDS
+// loads are complete before it, and no LDS access moves across it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Order of one MFMA sub-step's instructions: each of its 8 MFMAs is
+// followed by up to five VALU instructions (the dequantisation of the next
+// sub-step), the first four also by one LDS read (operands two sub-steps
+// ahead) and one global load.  A scheduling fence after every sub-step keeps
+// the reads two sub-steps ahead of their use.
+__device__ inline void schedule_substep() {
+#pragma unroll
+  for (int mi = 0; mi < kMB * kNB; ++mi) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+    if (mi < 4) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // global load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);             // VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Empty uses that make a value live at this point: the work that produces a
+// value carried into the next K step stays in the step that computes it
+// (the exit branch between steps would otherwise let the compiler sink it
+// into the next step, in front of that step's first MFMAs).
+__device__ inline void keep(const u32x4& v) { asm volatile("" ::"v"(v)); }
+__device__ inline void keep(const f16x8& v) { asm volatile("" ::"v"(v)); }
+__device__ inline void keep(uint32_t v) { asm volatile("" ::"v"(v)); }
+
+// SALIGN: every row's scales start on a 16-byte boundary (K / G a multiple
+// of 8 and a 16-byte aligned scale array), so they come in LDS windows;
+// otherwise with the stages.
+template <int G, bool KTAIL, bool SALIGN>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
             const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
-            int M, int N, int K, int gshift, int tiles_m, int tiles, int iters, int wg_per_xcd,
-            float* __restrict__ partials, uint32_t* __restrict__ flags) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2 * kATile];
+            int M, int N, int K, int tiles_m, int tiles_n, int iters, int rounds, int sk_tiles, int nsk,
+            float* __restrict__ partials, uint32_t* __restrict__ flags, uint32_t* __restrict__ counters) {
+  constexpr int kGroups = BK / G;            // scale groups per K step (1 or 4)
+  constexpr int kSBytes = SALIGN ? 0 : BN * kGroups * 4;       // per-stage scales (unaligned case)
+  constexpr int kStage = kStageBytes + kSBytes;
+  // one array per stage, so the compiler tracks loads into one stage apart
+  // from reads of another
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage2[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t swin[SALIGN ? 2 * kWinBytes : 16];   // scale windows
+  __shared__ __attribute__((aligned(16))) uint8_t sdummy[SALIGN ? 1024 : 16];          // idle window loads
   __shared__ int give_up;
+  auto stage = [&](int st) -> uint8_t* { return st == 0 ? stage0 : (st == 1 ? stage1 : stage2); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -97,89 +192,166 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 
   // Workgroups are dealt to XCDs round robin: XCD x runs ids x, x+8, ...
   const int wg = blockIdx.x;
+  const int wgs = gridDim.x;
   const int xcd = wg % kXCD;
   const int lwg = wg / kXCD;          // index among the XCD's workgroups
-  const int t_begin = xcd_tile_begin(xcd, tiles);
-  const int t_count = xcd_tile_begin(xcd + 1, tiles) - t_begin;
-  const long long xiters = (long long)t_count * iters;
-  const long long s_w = xiters * lwg / wg_per_xcd;
-  const long long e_w = xiters * (lwg + 1) / wg_per_xcd;
-  auto owner_start = [&](int l) { return xiters * l / wg_per_xcd; };
+  const int per_xcd = wgs / kXCD;
+
+  // This XCD's stream-K tiles and this workgroup's iteration range in them.
+  const int d_tiles = rounds * wgs;
+  const int sk_lo = xcd_begin(xcd, sk_tiles);
+  const int sk_cnt = xcd_begin(xcd + 1, sk_tiles) - sk_lo;
+  const long long sk_iters = (long long)sk_cnt * iters;
+  auto sk_start = [&](int l) -> long long { return sk_iters * l / nsk; };
+  const bool in_sk = lwg < nsk && sk_cnt > 0;
+  const long long my_s = in_sk ? sk_start(lwg) : 0, my_e = in_sk ? sk_start(lwg + 1) : 0;
+  const int n_seg = my_e > my_s ? (int)((my_e - 1) / iters - my_s / iters) + 1 : 0;   // 0, 1 or 2
+  const int j_first = (int)(my_s / iters);
 
   const uint32_t kbytes = (uint32_t)K * 2u;
+  const uint32_t wrow = (uint32_t)K >> 1;                      // packed bytes per weight row
+  const uint32_t spr = (uint32_t)K / (uint32_t)G;              // scales per weight row
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)M * kbytes);
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed, (uint32_t)N * ((uint32_t)K >> 1));
-  const uint32_t spr = (uint32_t)K >> (5 + gshift);   // scales per row
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed, (uint32_t)N * wrow);
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, (uint32_t)N * spr * 2u);
 
-  long long it = e_w;
-  while (it > s_w) {
-    // ---- the segment [a, b) of tile t that ends at `it`
-    const int tl = (int)((it - 1) / iters);                  // tile index within the XCD's range
-    const long long tile_lo = (long long)tl * iters;
-    const int a = (int)((s_w > tile_lo ? s_w : tile_lo) - tile_lo);
-    const int b = (int)(it - tile_lo);
-    const int t = t_begin + tl;
-    const int tm = t % tiles_m, tn = t / tiles_m;
+  // ---- LDS layouts and per-lane offsets (the same for every tile)
+  // Activations: row r of 256 bytes, 16-byte chunk c stored at c ^ (r % 16).
+  // Load j of wave w fills rows 16 j + 4 w .. + 3 (lane i: row + i / 16,
+  // stored chunk i % 16, so it fetches chunk (i % 16) ^ (row % 16)).
+  const int a_row = tid >> 4;                                   // + 16 j
+  const int a_chunk = (tid & 15) ^ (a_row & 15);
+  // Operand reads: sub-step s takes k = 64 h + 8 s .. + 8 of row 32 i + li.
+  uint32_t a_r[kSub];
+#pragma unroll
+  for (int s = 0; s < kSub; ++s) a_r[s] = (uint32_t)li * 256u + (uint32_t)(((8 * h + s) ^ (li & 15)) << 4);
+  // Weights: row n of 64 bytes, chunk c stored at c ^ ((n / 4) % 4).  Load j
+  // of wave w fills rows 64 j + 16 w .. + 15 (lane i: row + i / 4).
+  const int b_row = tid >> 2;                                   // + 64 j
+  const int b_chunk = (tid & 3) ^ ((b_row >> 2) & 3);
+  // Operand reads: lane (li, h) of column block nb takes k = 64 h .. + 64 of
+  // column 64 wave + 32 nb + li, as two chunks (half hf: sub-steps 4 hf ..).
+  uint32_t b_r[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+    b_r[hf] = (uint32_t)(wave * 64 + li) * 64u + (uint32_t)(((2 * h + hf) ^ ((li >> 2) & 3)) << 4);
+
+  // Stream-K segments first (their partials are then ready long before the
+  // fix-up), then the data-parallel tiles.
+  for (int item = 0; item < n_seg + rounds; ++item) {
+    const bool dp = item >= n_seg;
+    int tau, a, b;
+    if (!dp) {
+      const long long lo = (long long)(j_first + item) * iters;
+      a = (int)((my_s > lo ? my_s : lo) - lo);
+      b = (int)((my_e < lo + iters ? my_e : lo + iters) - lo);
+      tau = d_tiles + sk_lo + j_first + item;
+    } else {
+      tau = (item - n_seg) * wgs + xcd * per_xcd + lwg;
+      a = 0;
+      b = iters;
+    }
+    int tm, tn;
+    tile_coords(tau, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int nw = n0 + wave * kWaveN;
 
-    // Per-lane parts of the load offsets are fixed for the whole segment; the
-    // K step only moves the scalar offset.  A step past b gets a scalar
-    // offset outside every buffer (zeros, no memory access), and in a last
-    // step that covers only 32 of its 64 k the lanes beyond K get a
-    // per-lane offset outside the buffer -- selects, not branches, so the
-    // load counts stay fixed.
-    const int ktail = (K % BK) ? iters - 1 : iters;   // step whose upper half lies past K
-    // Per-lane parts of the load offsets are fixed for the whole segment; the
-    // K step only moves the scalar offset.  A step past b gets a scalar
-    // offset outside every buffer (zeros, no memory access), and in a last
-    // step that covers only 32 of its 64 k the lanes beyond K get a per-lane
-    // offset outside the buffer -- selects, not branches, so every step
-    // issues the same loads and the wait counts stay exact.
-    //
-    // A: thread t loads 4 chunks of 16 bytes per step: slot t + 256 j holds
-    // row r = slot / 8 at physical column c' = slot % 8 and is fetched from
-    // the row's logical chunk c = c' ^ swz(r).
-    uint32_t avoff[4], avoff_tail[4];
+    // Global offsets: per-lane row parts (rows past M or N get an offset
+    // outside the buffer: zeros, no memory access); the K step moves the
+    // scalar offset.  In the last step of a K that is not a multiple of 128,
+    // chunks past K are also sent outside the buffer.
+    uint32_t a_g[8], b_g[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = m0 + a_row + 16 * j;
+      a_g[j] = row < M ? (uint32_t)row * kbytes + (uint32_t)a_chunk * 16u : kOutOfRange;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int slot = tid + j * kThreads;
-      const int row = slot >> 3, c = (slot & 7) ^ swz(row);
-      avoff[j] = (m0 + row < M) ? (uint32_t)(m0 + row) * kbytes + (uint32_t)c * 16u : kOutOfRange;
-      avoff_tail[j] = c < 4 ? avoff[j] : kOutOfRange;
+      const int row = n0 + b_row + 64 * j;
+      b_g[j] = row < N ? (uint32_t)row * wrow + (uint32_t)b_chunk * 16u : kOutOfRange;
     }
-    auto load_a = [&](int kt, u32x4 (&ra)[4]) {
-      const uint32_t soff = kt < b ? (uint32_t)kt * (BK * 2) : kOutOfRange;
-      const bool tail = kt == ktail;
+    const int ktail = KTAIL ? iters - 1 : -1;
+    const int krem = K - (iters - 1) * BK;                   // k in the last step
+    const bool a_tail_ok = a_chunk * 8 < krem, b_tail_ok = b_chunk * 32 < krem;
+
+    // Part p of step kt into LDS stage st: activations (p < 4: loads 2 p,
+    // 2 p + 1), weights (p = 4, 5: loads 2 (p - 4) ..), and without SALIGN
+    // the step's scales (p = 6).
+    auto load_part = [&](int kt, int st, int p) {
+      const bool tail = KTAIL && kt == ktail;
+      uint8_t* base = stage(st);
+      if (p < 4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ra[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              xres, tail ? avoff_tail[j] : avoff[j], soff, 0));
+        for (int j = 2 * p; j < 2 * p + 2; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, W4A16_LDS(base + (16 * j + 4 * wave) * 256), 16,
+                                                   (tail && !a_tail_ok) ? kOutOfRange : a_g[j],
+                                                   (uint32_t)kt * (BK * 2), 0, 0);
+      } else if (p < 6) {
+#pragma unroll
+        for (int j = 2 * (p - 4); j < 2 * (p - 4) + 2; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, W4A16_LDS(base + kABytes + (64 * j + 16 * wave) * 64), 16,
+                                                   (tail && !b_tail_ok) ? kOutOfRange : b_g[j],
+                                                   (uint32_t)kt * (BK / 2), 0, 0);
+      } else if (p == 6 && !SALIGN) {
+        // row n's kGroups scales at n * kGroups * 4; load q of wave v covers
+        // rows 64 v + 16 q .. (g 32, lane i: row + i / 4, group i % 4) or
+        // rows 64 v .. + 63 (g 128, lane i: row + i)
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+          const int row = kGroups == 1 ? 64 * wave + lane : 64 * wave + 16 * q + (lane >> 2);
+          const uint32_t grp = (uint32_t)(kt * kGroups + (kGroups == 1 ? 0 : (lane & 3)));
+          const uint32_t off = n0 + row < N && grp < spr ? ((uint32_t)(n0 + row) * spr + grp) * 2u : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(base + kStageBytes + (64 * wave + 16 * q) * kGroups * 4),
+                                                   2, off, 0, 0, 0);
+        }
+      }
     };
-    auto store_a = [&](int buf, const u32x4 (&ra)[4]) {
+    auto load_stage = [&](int kt, int st) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(As + buf * kATile + (tid + j * kThreads) * 16) = ra[j];
+      for (int p = 0; p < 7; ++p) load_part(kt, st, p);
     };
-    uint32_t bvoff[kNB], bvoff_tail[kNB], svoff[kNB];
+    auto read_a = [&](int st, int s, u32x4 (&dst)[kMB]) {
+      const uint8_t* base = stage(st);
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int n = nw + nb * 32 + li;
-      bvoff[nb] = n < N ? (uint32_t)n * ((uint32_t)K >> 1) + (uint32_t)h * 16u : kOutOfRange;
-      bvoff_tail[nb] = h == 0 ? bvoff[nb] : kOutOfRange;
-      svoff[nb] = n < N ? ((uint32_t)n * spr + (gshift == 0 ? (uint32_t)h : 0u)) * 2u : kOutOfRange;
-    }
-    auto load_b = [&](int kt, u32x4 (&rb)[kNB], uint32_t (&rs)[kNB]) {
-      const bool live = kt < b;
-      const uint32_t wsoff = live ? (uint32_t)kt * (BK / 2) : kOutOfRange;
-      const uint32_t ssoff = live ? (((uint32_t)kt * BK) >> (5 + gshift)) * 2u : kOutOfRange;
-      const bool tail = kt == ktail;
+      for (int i = 0; i < kMB; ++i) dst[i] = *reinterpret_cast<const u32x4*>(base + i * 8192 + a_r[s]);
+    };
+    auto read_b = [&](int st, int hf, u32x4 (&dst)[kNB]) {
+      const uint8_t* base = stage(st) + kABytes;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) dst[nb] = *reinterpret_cast<const u32x4*>(base + nb * 2048 + b_r[hf]);
+    };
+
+    // Scale windows (SALIGN): groups [8 w, 8 w + 8) of all 256 rows of the
+    // tile, [row][8 x 2 bytes] in buffer w % 2; wave v loads rows 64 v .. + 63
+    // (lane i: row 64 v + i, 16 bytes).
+    const int srow = n0 + 64 * wave + lane;
+    const uint32_t s_g = srow < N ? (uint32_t)srow * spr * 2u : kOutOfRange;
+    auto load_window = [&](int w, bool live) {
+      if constexpr (SALIGN)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(live ? swin + (w & 1) * kWinBytes + 64 * wave * 16 : sdummy),
+                                                 16, live ? s_g : kOutOfRange, (uint32_t)w * 16u, 0, 0);
+    };
+    auto window_of = [&](int kt) { return (kt * kGroups) >> 3; };
+    // the scales of half hf of step kt, held in stage st (group kt for g 128;
+    // 4 kt + 2 h + hf for g 32)
+    auto read_scale = [&](int kt, int st, int hf, uint32_t (&dst)[kNB]) {
+      const int w = window_of(kt);
+      const int e = kt * kGroups - 8 * w + (kGroups == 1 ? 0 : 2 * h + hf);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        rb[nb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               wres, tail ? bvoff_tail[nb] : bvoff[nb], wsoff, kStream));
-        rs[nb] = __builtin_amdgcn_raw_buffer_load_b16(sres, svoff[nb], ssoff, 0);
+        const int row = wave * 64 + nb * 32 + li;
+        const uint8_t* p = SALIGN ? swin + (w & 1) * kWinBytes + row * 16 + e * 2
+                                  : stage(st) + kStageBytes + row * (kGroups * 4) + (kGroups == 1 ? 0 : (2 * h + hf) * 4);
+        dst[nb] = *reinterpret_cast<const uint16_t*>(p);
+      }
+    };
+    auto dequant = [&](const u32x4 (&w)[kNB], const uint32_t (&sc)[kNB], int word, f16x8 (&dst)[kNB]) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const uint32_t q = word == 0 ? w[nb].x : (word == 1 ? w[nb].y : (word == 2 ? w[nb].z : w[nb].w));
+        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[nb]);
+        dst[nb] = dequant_word_natural(q, f16x2{sv, sv});
       }
     };
 
@@ -189,83 +361,93 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) acc[i][nb] = f32x16{};
 
-    u32x4 ra[kAhead][4];
-    u32x4 rb[kAhead][kNB];
-    uint32_t rs[kAhead][kNB];
-#pragma unroll
-    for (int u = 0; u < kAhead; ++u) {
-      load_a(a + u, ra[u]);
-      load_b(a + u, rb[u], rs[u]);
-    }
-    store_a(0, ra[0]);
-    __syncthreads();
+    // Registers carried across sub-steps: activation operands three deep
+    // (sub-step g uses slot g % 3), the step's packed words and scales in two
+    // halves (sub-steps 0-3 and 4-7), and the dequantised weights of the
+    // current and the next sub-step.
+    u32x4 aop[3][kMB];
+    u32x4 bw[2][kNB];
+    uint32_t sc[2][kNB];
+    f16x8 bop[2][kNB];
 
-    // The step count is padded to a multiple of the unroll: a padding step
-    // reads only zeros, so it adds exactly nothing, and the unrolled body has
-    // no branches.
-    for (int base = a; base < b; base += kUnroll) {
+    const int nsteps = b - a;
+    auto clamp = [&](int r) { return a + (r < nsteps ? r : nsteps - 1); };
+    // Prologue: the scale windows of steps 0 and later, steps 0 and 1 into
+    // stages 0 and 1.  (Both window buffers may still be read by the
+    // previous tile until the barrier that ended its last step: passed.)
+    load_window(window_of(a), true);
+    load_window(window_of(a) + 1, true);
+    load_stage(clamp(0), 0);
+    load_stage(clamp(1), 1);
+    lds_barrier();
+    read_a(0, 0, aop[0]);
+    read_a(0, 1, aop[1]);
+    read_b(0, 0, bw[0]);
+    read_scale(a, 0, 0, sc[0]);
+    dequant(bw[0], sc[0], 0, bop[0]);
+
+    // One K step r (stage r % 3 == U).  Runs the 8 sub-steps and, spread over
+    // the first six, loads step r + 2 into the stage that step r - 1 used;
+    // the barrier at its end publishes step r + 2 (read from the next step on).
+    auto step = [&](auto u_tag, int r) {
+      constexpr int U = decltype(u_tag)::value;
+      constexpr int st_cur = U, st_nxt = (U + 1) % 3, st_ld = (U + 2) % 3;
+      const int kt = a + r;
+      // The first step of a window (other than the tile's first) loads the
+      // next window; the buffer it fills was last read in the step before.
+      const bool win_load = r > 0 && window_of(kt) != window_of(kt - 1);
+      load_window(window_of(kt) + 1, win_load);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int kt = base + u;
-        const int slot = u % kAhead;          // register ring slot of step kt
-        const uint8_t* at = As + (u & 1) * kATile;
-        // All 16 operand reads of the step first, so their LDS latencies
-        // overlap; the MFMAs then wait only for the reads they use.
-        u32x4 av[BK / 16][kMB];
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s)
-#pragma unroll
-          for (int i = 0; i < kMB; ++i) {
-            const int row = i * 32 + li;
-            const int c = 4 * h + s;              // logical 16-byte chunk of the row
-            av[s][i] = *reinterpret_cast<const u32x4*>(at + row * (BK * 2) + ((c ^ swz(row)) << 4));
-          }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-          f16x8 bop[kNB];
-#pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) {
-            const u32x4 w = rb[slot][nb];
-            const uint32_t q = s == 0 ? w.x : (s == 1 ? w.y : (s == 2 ? w.z : w.w));
-            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)rs[slot][nb]);
-            bop[nb] = dequant_word_natural(q, f16x2{sv, sv});
-          }
-#pragma unroll
-          for (int i = 0; i < kMB; ++i) {
-            const f16x8 aop = __builtin_bit_cast(f16x8, av[s][i]);
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
-              acc[i][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[nb], acc[i][nb], 0, 0, 0);
-          }
+      for (int s = 0; s < kSub; ++s) {
+        const int g = 2 * U + s;            // sub-step index mod 3 (8 = 2 mod 3)
+        load_part(clamp(r + 2), st_ld, s);
+        if (s + 2 < kSub) read_a(st_cur, s + 2, aop[(g + 2) % 3]);
+        else read_a(st_nxt, s + 2 - kSub, aop[(g + 2) % 3]);
+        if (s == 1) {
+          read_b(st_cur, 1, bw[1]);
+          read_scale(kt, st_cur, 1, sc[1]);
         }
-        store_a((u + 1) & 1, ra[(u + 1) % kAhead]);      // step kt + 1's activations into the other buffer
-        load_a(kt + kAhead, ra[slot]);                    // refill the ring
-        load_b(kt + kAhead, rb[slot], rs[slot]);
-        __syncthreads();
+        if (s == 4) {
+          read_b(st_nxt, 0, bw[0]);
+          read_scale(kt + 1, st_nxt, 0, sc[0]);
+        }
+        if (s + 1 < kSub) dequant(bw[(s + 1) >> 2], sc[(s + 1) >> 2], (s + 1) & 3, bop[(s + 1) & 1]);
+        else dequant(bw[0], sc[0], 0, bop[0]);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+          const f16x8 av = __builtin_bit_cast(f16x8, aop[g % 3][i]);
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb)
+            acc[i][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bop[s & 1][nb], acc[i][nb], 0, 0, 0);
+        }
+        schedule_substep();
       }
-    }
-    __builtin_amdgcn_s_waitcnt(0);            // drain the loads past the segment (zeros, no memory access)
-
-    // ---- partial or finished tile
-    // slot wg: the partial this workgroup publishes (at most one per call);
-    // slot wgs + wg: where a finisher parks its own accumulators while it sums
-    float* my_part = partials + (size_t)(b < iters ? wg : (int)gridDim.x + wg) * (kPartialBytes / 4);
-    auto store_partial = [&]() {
+      // operands of the next step's first two sub-steps
+      constexpr int g0 = (2 * (U + 1)) % 3;
 #pragma unroll
-      for (int i = 0; i < kMB; ++i)
+      for (int i = 0; i < kMB; ++i) {
+        keep(aop[g0][i]);
+        keep(aop[(g0 + 1) % 3][i]);
+      }
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          *reinterpret_cast<f32x16*>(my_part + ((size_t)((i * kNB + nb) * kThreads + tid) * 16)) = acc[i][nb];
+      for (int nb = 0; nb < kNB; ++nb) {
+        keep(bw[0][nb]);
+        keep(sc[0][nb]);
+        keep(bop[0][nb]);
+      }
+      lds_barrier();
     };
-    if (b < iters) {
-      // not the tile's last K step: publish the partial for the finisher
-      store_partial();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0) __hip_atomic_store(flags + wg, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (a == 0) {
-      // the whole tile is ours: convert straight from the accumulators.
+
+    for (int r = 0;;) {
+      step(std::integral_constant<int, 0>{}, r);
+      if (++r == nsteps) break;
+      step(std::integral_constant<int, 1>{}, r);
+      if (++r == nsteps) break;
+      step(std::integral_constant<int, 2>{}, r);
+      if (++r == nsteps) break;
+    }
+
+    if (dp) {
       // lane holds column li of each block, rows 8*(r/4) + 4*h + r%4
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
@@ -281,54 +463,90 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
         }
       }
     } else {
-      // Lower-numbered workgroups of this XCD hold the K steps [0, a), each
-      // as the first segment it computed (one that needs no waiting).  Park
-      // our own partial, wait for theirs, then sum: ours first, then theirs
-      // nearest first (a fixed order, so the result is deterministic).
-      store_partial();
-      if (tid == 0) give_up = 0;
+      // publish the partial (slot 2 wg + item) for the fix-up
+      float* part = partials + (size_t)(2 * wg + item) * (kPartialBytes / 4);
+#pragma unroll
+      for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          *reinterpret_cast<f32x16*>(part + ((size_t)((i * kNB + nb) * kThreads + tid) * 16)) = acc[i][nb];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __syncthreads();
-      if (tid == 0) {
-        for (int l = lwg - 1; l >= 0 && owner_start(l + 1) > tile_lo; --l) {
-          if (owner_start(l) == owner_start(l + 1)) continue;   // empty range: no partial
-          uint32_t spins = 0;
-          while (__hip_atomic_load(flags + l * kXCD + xcd, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins == kSpinLimit) { give_up = 1; break; }
-          }
+      if (tid == 0) __hip_atomic_store(flags + 2 * wg + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // ---- fix-up: each contributor of a stream-K tile reduces one slice of it.
+  // Wait for every partial of both segments first (relaxed polls), then one
+  // acquire fence makes them all visible.
+  if (n_seg == 0) return;
+  if (tid == 0) {
+    give_up = 0;
+    for (int e = 0; e < n_seg; ++e) {
+      const long long lo = (long long)(j_first + e) * iters, hi = lo + iters;
+      for (int l = 0; l < nsk; ++l) {
+        const long long s0 = sk_start(l), s1 = sk_start(l + 1);
+        if (!(s1 > s0 && s0 < hi && s1 > lo)) continue;
+        const int slot = 2 * (l * kXCD + xcd) + (s0 < lo ? 1 : 0);
+        uint32_t spins = 0;
+        while (__hip_atomic_load(flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins == kSpinLimit) { give_up = 1; break; }
         }
-      }
-      __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      const bool failed = give_up != 0;
-#pragma unroll
-      for (int i = 0; i < kMB; ++i) {
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const size_t off = (size_t)((i * kNB + nb) * kThreads + tid) * 16;
-          f32x16 v = *reinterpret_cast<const f32x16*>(my_part + off);
-          for (int l = lwg - 1; l >= 0 && owner_start(l + 1) > tile_lo; --l) {
-            if (owner_start(l) == owner_start(l + 1)) continue;
-            v += *reinterpret_cast<const f32x16*>(partials + (size_t)(l * kXCD + xcd) * (kPartialBytes / 4) + off);
-          }
-          const int n = nw + nb * 32 + li;
-          if (n < N) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-              if (m < M) y[(size_t)m * N + n] = failed ? (uint16_t)0x7E00u : float_to_half_bits(v[r]);
-            }
-          }
-        }
-      }
-      __syncthreads();
-      if (tid == 0) {
-        for (int l = lwg - 1; l >= 0 && owner_start(l + 1) > tile_lo; --l)
-          if (owner_start(l) != owner_start(l + 1))
-            __hip_atomic_store(flags + l * kXCD + xcd, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    it = tile_lo + a;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const bool failed = give_up != 0;
+  for (int e = 0; e < n_seg; ++e) {
+    const int j = j_first + e;
+    const long long lo = (long long)j * iters, hi = lo + iters;
+    int c0 = -1, c1 = -1;                     // contributors: this XCD's workgroups c0 .. c1
+    for (int l = 0; l < nsk; ++l) {
+      const long long s0 = sk_start(l), s1 = sk_start(l + 1);
+      if (s1 > s0 && s0 < hi && s1 > lo) {
+        if (c0 < 0) c0 = l;
+        c1 = l;
+      }
+    }
+    const int parts = c1 - c0 + 1;
+    // the partial of contributor l for tile j: its second segment if its range began earlier
+    auto slot = [&](int l) { return 2 * (l * kXCD + xcd) + (sk_start(l) < lo ? 1 : 0); };
+    int tm, tn;
+    tile_coords(d_tiles + sk_lo + j, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    // slice: f32x16 chunks [ch0, ch1) of the partial layout (i, nb, thread)
+    constexpr int kChunks = kMB * kNB * kThreads;
+    const int q = lwg - c0;
+    const int ch0 = kChunks * q / parts, ch1 = kChunks * (q + 1) / parts;
+    for (int c = ch0 + tid; c < ch1; c += kThreads) {
+      f32x16 v = *reinterpret_cast<const f32x16*>(partials + (size_t)slot(c0) * (kPartialBytes / 4) + (size_t)c * 16);
+      for (int l = c0 + 1; l <= c1; ++l)
+        v += *reinterpret_cast<const f32x16*>(partials + (size_t)slot(l) * (kPartialBytes / 4) + (size_t)c * 16);
+      const int t = c % kThreads, blk = c / kThreads;
+      const int i = blk / kNB, nb = blk % kNB;
+      const int cl = t & 63, ch = cl >> 5;
+      const int n = n0 + (t >> 6) * kWaveN + nb * 32 + (cl & 31);
+      if (n < N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * ch + (r & 3);
+          if (m < M) y[(size_t)m * N + n] = failed ? (uint16_t)0x7E00u : float_to_half_bits(v[r]);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      // the last contributor to finish reading clears the tile's flags
+      const uint32_t done = __hip_atomic_fetch_add(counters + xcd * per_xcd + j, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (done == (uint32_t)parts - 1u) {
+        for (int l = c0; l <= c1; ++l)
+          __hip_atomic_store(flags + slot(l), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(counters + xcd * per_xcd + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -336,17 +554,29 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int, const DeviceInfo& dev) {
   const GemmPlan p = gemm_plan((int)m, (int)n, (int)k, dev);
-  return 2 * (size_t)p.wgs * kPartialBytes + (size_t)p.wgs * sizeof(uint32_t);
+  if (p.sk_tiles == 0) return 0;
+  // two partial slots and two flags per workgroup, one counter per stream-K tile slot
+  return 2 * (size_t)p.wgs * kPartialBytes + 3 * (size_t)p.wgs * sizeof(uint32_t);
 }
 
 hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                        int n, int k, int group, void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   const GemmPlan p = gemm_plan(m, n, k, dev);
-  const int gshift = group == 128 ? 2 : 0;
   float* partials = static_cast<float*>(workspace);
-  uint32_t* flags = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + 2 * (size_t)p.wgs * kPartialBytes);
-  hipLaunchKernelGGL(gemm_kernel, dim3(p.wgs), dim3(kThreads), 0, stream, x, packed, scales, y, m, n, k, gshift,
-                     p.tiles_m, p.tiles, p.iters, p.wg_per_xcd, partials, flags);
+  uint32_t* flags = nullptr;
+  uint32_t* counters = nullptr;
+  if (workspace) {
+    flags = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + 2 * (size_t)p.wgs * kPartialBytes);
+    counters = flags + 2 * (size_t)p.wgs;
+  }
+  const bool tail = k % BK != 0;
+  const bool salign = (k / group) % 8 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
+  auto kern = group == 128 ? (salign ? gemm_kernel<128, false, true> : gemm_kernel<128, false, false>)
+              : tail       ? gemm_kernel<32, true, false>
+              : salign     ? gemm_kernel<32, false, true>
+                           : gemm_kernel<32, false, false>;
+  hipLaunchKernelGGL(kern, dim3(p.wgs), dim3(kThreads), 0, stream, x, packed, scales, y, m, n, k, p.tiles_m,
+                     p.tiles_n, p.iters, p.rounds, p.sk_tiles, p.nsk, partials, flags, counters);
   return hipGetLastError();
 }
 
