@@ -23,6 +23,12 @@ constexpr int kRawBufferFlags = 0x00020000;
 // Cache policy bit for data streamed exactly once (non-temporal).
 constexpr int kStream = 2;
 
+// Cache policy for data handed between workgroups on different CUs (and so,
+// on this multi-XCD part, possibly different L2s): device scope (sc1), so a
+// store reaches and a load reads the device coherence point, and no L2
+// write-back or invalidation is needed around the exchange.
+constexpr int kDeviceScope = 16;
+
 // An offset that lies outside every buffer: loads from it return 0.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 

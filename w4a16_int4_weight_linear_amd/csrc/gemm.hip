@@ -214,6 +214,10 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)M * kbytes);
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed, (uint32_t)N * wrow);
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, (uint32_t)N * spr * 2u);
+  // fp32 partial tiles: slot p at p * kPartialBytes; inside a slot, 16-byte
+  // quad q of accumulator block blk of thread t at ((blk * 4 + q) * 256 + t) * 16,
+  // so every store or load instruction covers 1 KB contiguously
+  const __amdgpu_buffer_rsrc_t pres = make_rsrc(partials, partials ? 2u * (uint32_t)wgs * (uint32_t)kPartialBytes : 0u);
 
   // ---- LDS layouts and per-lane offsets (the same for every tile)
   // Activations: row r of 256 bytes, 16-byte chunk c stored at c ^ (r % 16).
@@ -463,22 +467,29 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
         }
       }
     } else {
-      // publish the partial (slot 2 wg + item) for the fix-up
-      float* part = partials + (size_t)(2 * wg + item) * (kPartialBytes / 4);
+      // Publish the partial (slot 2 wg + item) for the fix-up: device-scope
+      // stores, all complete (s_waitcnt) before the flag is raised.
+      const uint32_t slot_off = (uint32_t)(2 * wg + item) * (uint32_t)kPartialBytes;
 #pragma unroll
       for (int i = 0; i < kMB; ++i)
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          *reinterpret_cast<f32x16*>(part + ((size_t)((i * kNB + nb) * kThreads + tid) * 16)) = acc[i][nb];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = {acc[i][nb][4 * q], acc[i][nb][4 * q + 1], acc[i][nb][4 * q + 2], acc[i][nb][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), pres,
+                                                   (uint32_t)((((i * kNB + nb) * 4 + q) * kThreads + tid) * 16),
+                                                   slot_off, kDeviceScope);
+          }
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) __hip_atomic_store(flags + 2 * wg + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
   // ---- fix-up: each contributor of a stream-K tile reduces one slice of it.
-  // Wait for every partial of both segments first (relaxed polls), then one
-  // acquire fence makes them all visible.
+  // Wait for every partial of both segments first (relaxed device-scope
+  // polls); the partials are then read with device-scope loads.
   if (n_seg == 0) return;
   if (tid == 0) {
     give_up = 0;
@@ -497,7 +508,6 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     }
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const bool failed = give_up != 0;
   for (int e = 0; e < n_seg; ++e) {
     const int j = j_first + e;
@@ -516,22 +526,27 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     int tm, tn;
     tile_coords(d_tiles + sk_lo + j, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    // slice: f32x16 chunks [ch0, ch1) of the partial layout (i, nb, thread)
-    constexpr int kChunks = kMB * kNB * kThreads;
-    const int q = lwg - c0;
-    const int ch0 = kChunks * q / parts, ch1 = kChunks * (q + 1) / parts;
+    // slice: 16-byte quads [ch0, ch1) of the partial layout (blk, q, thread)
+    constexpr int kChunks = kMB * kNB * 4 * kThreads;
+    const int qs = lwg - c0;
+    const int ch0 = kChunks * qs / parts, ch1 = kChunks * (qs + 1) / parts;
     for (int c = ch0 + tid; c < ch1; c += kThreads) {
-      f32x16 v = *reinterpret_cast<const f32x16*>(partials + (size_t)slot(c0) * (kPartialBytes / 4) + (size_t)c * 16);
+      f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              pres, (uint32_t)c * 16u, (uint32_t)slot(c0) * (uint32_t)kPartialBytes,
+                                              kDeviceScope));
       for (int l = c0 + 1; l <= c1; ++l)
-        v += *reinterpret_cast<const f32x16*>(partials + (size_t)slot(l) * (kPartialBytes / 4) + (size_t)c * 16);
-      const int t = c % kThreads, blk = c / kThreads;
+        v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           pres, (uint32_t)c * 16u, (uint32_t)slot(l) * (uint32_t)kPartialBytes,
+                                           kDeviceScope));
+      const int t = c % kThreads, bq = c / kThreads;
+      const int blk = bq >> 2, q = bq & 3;
       const int i = blk / kNB, nb = blk % kNB;
       const int cl = t & 63, ch = cl >> 5;
       const int n = n0 + (t >> 6) * kWaveN + nb * 32 + (cl & 31);
       if (n < N) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * ch + (r & 3);
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + i * 32 + 8 * q + 4 * ch + r;
           if (m < M) y[(size_t)m * N + n] = failed ? (uint16_t)0x7E00u : float_to_half_bits(v[r]);
         }
       }
