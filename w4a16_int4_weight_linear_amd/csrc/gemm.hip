@@ -97,6 +97,7 @@ GemmPlan gemm_plan(int m, int n, int k, const DeviceInfo& dev) {
   p.iters = (k + BK - 1) / BK;
   int per_xcd = (dev.num_cu * kWGPerCU) / kXCD;
   if (per_xcd < 1) per_xcd = 1;
+  if (per_xcd > 64) per_xcd = 64;           // the fix-up polls one contributor per lane
   p.wgs = per_xcd * kXCD;
   p.rounds = p.tiles / p.wgs;
   p.sk_tiles = p.tiles - p.rounds * p.wgs;
@@ -488,56 +489,76 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   }
 
   // ---- fix-up: each contributor of a stream-K tile reduces one slice of it.
-  // Wait for every partial of both segments first (relaxed device-scope
-  // polls); the partials are then read with device-scope loads.
   if (n_seg == 0) return;
-  if (tid == 0) {
-    give_up = 0;
+  // Wave 0 builds the table of this workgroup's one or two stream-K tiles:
+  // lane l describes the XCD's workgroup l (nsk <= 64) and polls its flag.
+  __shared__ uint32_t fix_slot[2][64];       // partial slot of each contributor
+  __shared__ int fix_c0[2], fix_c1[2];
+  if (wave == 0) {
+    const long long s0 = lane < nsk ? sk_start(lane) : 0, s1 = lane < nsk ? sk_start(lane + 1) : 0;
+    bool pending = false;
     for (int e = 0; e < n_seg; ++e) {
       const long long lo = (long long)(j_first + e) * iters, hi = lo + iters;
-      for (int l = 0; l < nsk; ++l) {
-        const long long s0 = sk_start(l), s1 = sk_start(l + 1);
-        if (!(s1 > s0 && s0 < hi && s1 > lo)) continue;
-        const int slot = 2 * (l * kXCD + xcd) + (s0 < lo ? 1 : 0);
-        uint32_t spins = 0;
-        while (__hip_atomic_load(flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins == kSpinLimit) { give_up = 1; break; }
+      const bool mine = lane < nsk && s1 > s0 && s0 < hi && s1 > lo;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(mine);
+      // second segment of its range if the range began before this tile
+      const uint32_t slot = 2u * (uint32_t)(lane * kXCD + xcd) + (s0 < lo ? 1u : 0u);
+      if (mine) fix_slot[e][lane] = slot;
+      if (lane == 0) {
+        fix_c0[e] = (int)__builtin_ctzll(m);
+        fix_c1[e] = 63 - (int)__builtin_clzll(m);
+      }
+      pending = pending || mine;
+    }
+    // wait until every contributor of both tiles has raised its flag
+    uint32_t spins = 0;
+    bool failed_poll = false;
+    for (;;) {
+      bool missing = false;
+      for (int e = 0; e < n_seg; ++e) {
+        const long long lo = (long long)(j_first + e) * iters, hi = lo + iters;
+        const bool mine = lane < nsk && s1 > s0 && s0 < hi && s1 > lo;
+        if (mine) {
+          const uint32_t slot = 2u * (uint32_t)(lane * kXCD + xcd) + (s0 < lo ? 1u : 0u);
+          missing = missing || __hip_atomic_load(flags + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
         }
       }
+      if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == kSpinLimit) { failed_poll = true; break; }
     }
+    (void)pending;
+    if (lane == 0) give_up = failed_poll ? 1 : 0;
   }
   __syncthreads();
   const bool failed = give_up != 0;
   for (int e = 0; e < n_seg; ++e) {
     const int j = j_first + e;
-    const long long lo = (long long)j * iters, hi = lo + iters;
-    int c0 = -1, c1 = -1;                     // contributors: this XCD's workgroups c0 .. c1
-    for (int l = 0; l < nsk; ++l) {
-      const long long s0 = sk_start(l), s1 = sk_start(l + 1);
-      if (s1 > s0 && s0 < hi && s1 > lo) {
-        if (c0 < 0) c0 = l;
-        c1 = l;
-      }
-    }
+    const int c0 = fix_c0[e], c1 = fix_c1[e];
     const int parts = c1 - c0 + 1;
-    // the partial of contributor l for tile j: its second segment if its range began earlier
-    auto slot = [&](int l) { return 2 * (l * kXCD + xcd) + (sk_start(l) < lo ? 1 : 0); };
     int tm, tn;
     tile_coords(d_tiles + sk_lo + j, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    // slice: 16-byte quads [ch0, ch1) of the partial layout (blk, q, thread)
+    // slice: 16-byte quads [ch0, ch1) of the partial layout (blk, q, thread);
+    // the contributors' quads are summed in contributor order, 8 loads in flight
     constexpr int kChunks = kMB * kNB * 4 * kThreads;
     const int qs = lwg - c0;
     const int ch0 = kChunks * qs / parts, ch1 = kChunks * (qs + 1) / parts;
     for (int c = ch0 + tid; c < ch1; c += kThreads) {
-      f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              pres, (uint32_t)c * 16u, (uint32_t)slot(c0) * (uint32_t)kPartialBytes,
-                                              kDeviceScope));
-      for (int l = c0 + 1; l <= c1; ++l)
-        v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           pres, (uint32_t)c * 16u, (uint32_t)slot(l) * (uint32_t)kPartialBytes,
-                                           kDeviceScope));
+      auto quad = [&](int l) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             pres, (uint32_t)c * 16u, fix_slot[e][l] * (uint32_t)kPartialBytes,
+                                             kDeviceScope));
+      };
+      f32x4 v = quad(c0);
+      for (int l0 = c0 + 1; l0 <= c1; l0 += 8) {
+        f32x4 pq[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pq[u] = quad(l0 + u <= c1 ? l0 + u : c0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (l0 + u <= c1) v += pq[u];
+      }
       const int t = c % kThreads, bq = c / kThreads;
       const int blk = bq >> 2, q = bq & 3;
       const int i = blk / kNB, nb = blk % kNB;
@@ -558,7 +579,7 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (done == (uint32_t)parts - 1u) {
         for (int l = c0; l <= c1; ++l)
-          __hip_atomic_store(flags + slot(l), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(flags + fix_slot[e][l], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(counters + xcd * per_xcd + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
