@@ -50,6 +50,17 @@ def _compile(hipcc: str, src: str) -> str:
     return obj
 
 
+def _check_resolves(path: str) -> None:
+    """Load the freshly linked library in a child process: a symbol of its own
+    that a source failed to define (for instance a kernel whose host stub
+    was not emitted) is an error here rather than at the first import."""
+    probe = f"import ctypes; ctypes.CDLL({path!r})"
+    r = subprocess.run([sys.executable, "-c", probe], capture_output=True, text=True)
+    if r.returncode != 0:
+        os.remove(path)
+        raise RuntimeError(f"linked library does not load: {r.stderr.strip().splitlines()[-1] if r.stderr else ''}")
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libw4a16.so; returns the library path."""
     hipcc = _hipcc()
@@ -62,6 +73,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    _check_resolves(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)

@@ -163,6 +163,13 @@ __device__ inline void keep(const u32x4& v) { asm volatile("" ::"v"(v)); }
 __device__ inline void keep(const f16x8& v) { asm volatile("" ::"v"(v)); }
 __device__ inline void keep(uint32_t v) { asm volatile("" ::"v"(v)); }
 
+// One work item of a workgroup: a stream-K segment [a, b) of the tile at
+// (m0, n0), or the whole tile (dp).
+struct Item {
+  int a, b, m0, n0;
+  bool dp;
+};
+
 // SALIGN: every row's scales start on a 16-byte boundary (K / G a multiple
 // of 8 and a 16-byte aligned scale array), so they come in LDS windows;
 // otherwise with the stages.
@@ -241,124 +248,138 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   for (int hf = 0; hf < 2; ++hf)
     b_r[hf] = (uint32_t)(wave * 64 + li) * 64u + (uint32_t)(((2 * h + hf) ^ ((li >> 2) & 3)) << 4);
 
-  // Stream-K segments first (their partials are then ready long before the
-  // fix-up), then the data-parallel tiles.
-  for (int item = 0; item < n_seg + rounds; ++item) {
-    const bool dp = item >= n_seg;
-    int tau, a, b;
-    if (!dp) {
+  const int ktail = KTAIL ? iters - 1 : -1;
+  const int krem = K - (iters - 1) * BK;                     // k in the last step
+  const bool a_tail_ok = a_chunk * 8 < krem, b_tail_ok = b_chunk * 32 < krem;
+
+  // Global offsets: the per-lane part (row within the tile, chunk) is the
+  // same for every tile; the tile's first row and the K step go into the
+  // scalar offset.  The range check covers the sum, so rows past M or N read
+  // zeros (or, where the 32-bit offset wraps, other data of the same buffer:
+  // such rows only feed outputs that are never stored).
+  const uint32_t a_v = (uint32_t)a_row * kbytes + (uint32_t)a_chunk * 16u;
+  const uint32_t b_v = (uint32_t)b_row * wrow + (uint32_t)b_chunk * 16u;
+  const uint32_t s_v = (uint32_t)(64 * wave + lane) * spr * 2u;
+  auto setup = [&](int item) {
+    Item it;
+    it.dp = item >= n_seg;
+    int tau;
+    if (!it.dp) {
       const long long lo = (long long)(j_first + item) * iters;
-      a = (int)((my_s > lo ? my_s : lo) - lo);
-      b = (int)((my_e < lo + iters ? my_e : lo + iters) - lo);
+      it.a = (int)((my_s > lo ? my_s : lo) - lo);
+      it.b = (int)((my_e < lo + iters ? my_e : lo + iters) - lo);
       tau = d_tiles + sk_lo + j_first + item;
     } else {
       tau = (item - n_seg) * wgs + xcd * per_xcd + lwg;
-      a = 0;
-      b = iters;
+      it.a = 0;
+      it.b = iters;
     }
     int tm, tn;
     tile_coords(tau, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    it.m0 = tm * BM;
+    it.n0 = tn * BN;
+    return it;
+  };
+
+  // Part p of step kt into LDS stage st: activations (p < 4: loads 2 p,
+  // 2 p + 1), weights (p = 4, 5: loads 2 (p - 4) ..), and without SALIGN the
+  // step's scales (p = 6).  In the last step of a K that is not a multiple of
+  // 128, chunks and groups past K are sent outside the buffer.
+  auto load_part = [&](const Item& it, int kt, int st, int p) {
+    const bool tail = KTAIL && kt == ktail;
+    uint8_t* base = stage(st);
+    if (p < 4) {
+#pragma unroll
+      for (int j = 2 * p; j < 2 * p + 2; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, W4A16_LDS(base + (16 * j + 4 * wave) * 256), 16,
+                                                 (tail && !a_tail_ok) ? kOutOfRange : a_v,
+                                                 (uint32_t)(it.m0 + 16 * j) * kbytes + (uint32_t)kt * (BK * 2), 0, 0);
+    } else if (p < 6) {
+#pragma unroll
+      for (int j = 2 * (p - 4); j < 2 * (p - 4) + 2; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, W4A16_LDS(base + kABytes + (64 * j + 16 * wave) * 64), 16,
+                                                 (tail && !b_tail_ok) ? kOutOfRange : b_v,
+                                                 (uint32_t)(it.n0 + 64 * j) * wrow + (uint32_t)kt * (BK / 2), 0, 0);
+    } else if (p == 6 && !SALIGN) {
+      // row n's kGroups scales at n * kGroups * 4; load q of wave v covers
+      // rows 64 v + 16 q .. (g 32, lane i: row + i / 4, group i % 4) or
+      // rows 64 v .. + 63 (g 128, lane i: row + i)
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) {
+        const int row = kGroups == 1 ? 64 * wave + lane : 64 * wave + 16 * q + (lane >> 2);
+        const uint32_t grp = (uint32_t)(kt * kGroups + (kGroups == 1 ? 0 : (lane & 3)));
+        const uint32_t off = it.n0 + row < N && grp < spr ? ((uint32_t)(it.n0 + row) * spr + grp) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(base + kStageBytes + (64 * wave + 16 * q) * kGroups * 4),
+                                                 2, off, 0, 0, 0);
+      }
+    }
+  };
+  auto load_stage = [&](const Item& it, int kt, int st) {
+#pragma unroll
+    for (int p = 0; p < 7; ++p) load_part(it, kt, st, p);
+  };
+  // Scale windows (SALIGN): groups [8 w, 8 w + 8) of all 256 rows of the
+  // tile, [row][8 x 2 bytes] in buffer w % 2; wave v loads rows 64 v .. + 63
+  // (lane i: row 64 v + i, 16 bytes).
+  auto load_window = [&](const Item& it, int w, bool live) {
+    if constexpr (SALIGN)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(live ? swin + (w & 1) * kWinBytes + 64 * wave * 16 : sdummy),
+                                               16, live ? s_v : kOutOfRange, (uint32_t)it.n0 * spr * 2u + (uint32_t)w * 16u,
+                                               0, 0);
+  };
+  auto window_of = [&](int kt) { return (kt * kGroups) >> 3; };
+  auto clamp_of = [&](const Item& it, int r) { return it.a + (r < it.b - it.a ? r : it.b - it.a - 1); };
+  // The loads an item needs before its first step: its first scale windows
+  // and steps 0 and 1 (stages 0 and 1).
+  auto prologue_loads = [&](const Item& it) {
+    load_window(it, window_of(it.a), true);
+    load_window(it, window_of(it.a) + 1, true);
+    load_stage(it, clamp_of(it, 0), 0);
+    load_stage(it, clamp_of(it, 1), 1);
+  };
+  auto read_a = [&](int st, int s, u32x4 (&dst)[kMB]) {
+    const uint8_t* base = stage(st);
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) dst[i] = *reinterpret_cast<const u32x4*>(base + i * 8192 + a_r[s]);
+  };
+  auto read_b = [&](int st, int hf, u32x4 (&dst)[kNB]) {
+    const uint8_t* base = stage(st) + kABytes;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) dst[nb] = *reinterpret_cast<const u32x4*>(base + nb * 2048 + b_r[hf]);
+  };
+  // the scales of half hf of step kt, held in stage st (group kt for g 128;
+  // 4 kt + 2 h + hf for g 32)
+  auto read_scale = [&](int kt, int st, int hf, uint32_t (&dst)[kNB]) {
+    const int w = window_of(kt);
+    const int e = kt * kGroups - 8 * w + (kGroups == 1 ? 0 : 2 * h + hf);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int row = wave * 64 + nb * 32 + li;
+      const uint8_t* p = SALIGN ? swin + (w & 1) * kWinBytes + row * 16 + e * 2
+                                : stage(st) + kStageBytes + row * (kGroups * 4) + (kGroups == 1 ? 0 : (2 * h + hf) * 4);
+      dst[nb] = *reinterpret_cast<const uint16_t*>(p);
+    }
+  };
+  auto dequant = [&](const u32x4 (&w)[kNB], const uint32_t (&sc)[kNB], int word, f16x8 (&dst)[kNB]) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const uint32_t q = word == 0 ? w[nb].x : (word == 1 ? w[nb].y : (word == 2 ? w[nb].z : w[nb].w));
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[nb]);
+      dst[nb] = dequant_word_natural(q, f16x2{sv, sv});
+    }
+  };
+
+  // Stream-K segments first (their partials are then ready long before the
+  // fix-up), then the data-parallel tiles.  The next item's first loads are
+  // issued before this item's results are written, so their latency
+  // overlaps the output work.
+  const int n_items = n_seg + rounds;
+  Item cur = setup(0);
+  if (n_items > 0) prologue_loads(cur);
+  for (int item = 0; item < n_items; ++item) {
+    const bool dp = cur.dp;
+    const int a = cur.a, b = cur.b, m0 = cur.m0, n0 = cur.n0;
     const int nw = n0 + wave * kWaveN;
-
-    // Global offsets: per-lane row parts (rows past M or N get an offset
-    // outside the buffer: zeros, no memory access); the K step moves the
-    // scalar offset.  In the last step of a K that is not a multiple of 128,
-    // chunks past K are also sent outside the buffer.
-    uint32_t a_g[8], b_g[4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = m0 + a_row + 16 * j;
-      a_g[j] = row < M ? (uint32_t)row * kbytes + (uint32_t)a_chunk * 16u : kOutOfRange;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = n0 + b_row + 64 * j;
-      b_g[j] = row < N ? (uint32_t)row * wrow + (uint32_t)b_chunk * 16u : kOutOfRange;
-    }
-    const int ktail = KTAIL ? iters - 1 : -1;
-    const int krem = K - (iters - 1) * BK;                   // k in the last step
-    const bool a_tail_ok = a_chunk * 8 < krem, b_tail_ok = b_chunk * 32 < krem;
-
-    // Part p of step kt into LDS stage st: activations (p < 4: loads 2 p,
-    // 2 p + 1), weights (p = 4, 5: loads 2 (p - 4) ..), and without SALIGN
-    // the step's scales (p = 6).
-    auto load_part = [&](int kt, int st, int p) {
-      const bool tail = KTAIL && kt == ktail;
-      uint8_t* base = stage(st);
-      if (p < 4) {
-#pragma unroll
-        for (int j = 2 * p; j < 2 * p + 2; ++j)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, W4A16_LDS(base + (16 * j + 4 * wave) * 256), 16,
-                                                   (tail && !a_tail_ok) ? kOutOfRange : a_g[j],
-                                                   (uint32_t)kt * (BK * 2), 0, 0);
-      } else if (p < 6) {
-#pragma unroll
-        for (int j = 2 * (p - 4); j < 2 * (p - 4) + 2; ++j)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, W4A16_LDS(base + kABytes + (64 * j + 16 * wave) * 64), 16,
-                                                   (tail && !b_tail_ok) ? kOutOfRange : b_g[j],
-                                                   (uint32_t)kt * (BK / 2), 0, 0);
-      } else if (p == 6 && !SALIGN) {
-        // row n's kGroups scales at n * kGroups * 4; load q of wave v covers
-        // rows 64 v + 16 q .. (g 32, lane i: row + i / 4, group i % 4) or
-        // rows 64 v .. + 63 (g 128, lane i: row + i)
-#pragma unroll
-        for (int q = 0; q < kGroups; ++q) {
-          const int row = kGroups == 1 ? 64 * wave + lane : 64 * wave + 16 * q + (lane >> 2);
-          const uint32_t grp = (uint32_t)(kt * kGroups + (kGroups == 1 ? 0 : (lane & 3)));
-          const uint32_t off = n0 + row < N && grp < spr ? ((uint32_t)(n0 + row) * spr + grp) * 2u : kOutOfRange;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(base + kStageBytes + (64 * wave + 16 * q) * kGroups * 4),
-                                                   2, off, 0, 0, 0);
-        }
-      }
-    };
-    auto load_stage = [&](int kt, int st) {
-#pragma unroll
-      for (int p = 0; p < 7; ++p) load_part(kt, st, p);
-    };
-    auto read_a = [&](int st, int s, u32x4 (&dst)[kMB]) {
-      const uint8_t* base = stage(st);
-#pragma unroll
-      for (int i = 0; i < kMB; ++i) dst[i] = *reinterpret_cast<const u32x4*>(base + i * 8192 + a_r[s]);
-    };
-    auto read_b = [&](int st, int hf, u32x4 (&dst)[kNB]) {
-      const uint8_t* base = stage(st) + kABytes;
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) dst[nb] = *reinterpret_cast<const u32x4*>(base + nb * 2048 + b_r[hf]);
-    };
-
-    // Scale windows (SALIGN): groups [8 w, 8 w + 8) of all 256 rows of the
-    // tile, [row][8 x 2 bytes] in buffer w % 2; wave v loads rows 64 v .. + 63
-    // (lane i: row 64 v + i, 16 bytes).
-    const int srow = n0 + 64 * wave + lane;
-    const uint32_t s_g = srow < N ? (uint32_t)srow * spr * 2u : kOutOfRange;
-    auto load_window = [&](int w, bool live) {
-      if constexpr (SALIGN)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(live ? swin + (w & 1) * kWinBytes + 64 * wave * 16 : sdummy),
-                                                 16, live ? s_g : kOutOfRange, (uint32_t)w * 16u, 0, 0);
-    };
-    auto window_of = [&](int kt) { return (kt * kGroups) >> 3; };
-    // the scales of half hf of step kt, held in stage st (group kt for g 128;
-    // 4 kt + 2 h + hf for g 32)
-    auto read_scale = [&](int kt, int st, int hf, uint32_t (&dst)[kNB]) {
-      const int w = window_of(kt);
-      const int e = kt * kGroups - 8 * w + (kGroups == 1 ? 0 : 2 * h + hf);
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int row = wave * 64 + nb * 32 + li;
-        const uint8_t* p = SALIGN ? swin + (w & 1) * kWinBytes + row * 16 + e * 2
-                                  : stage(st) + kStageBytes + row * (kGroups * 4) + (kGroups == 1 ? 0 : (2 * h + hf) * 4);
-        dst[nb] = *reinterpret_cast<const uint16_t*>(p);
-      }
-    };
-    auto dequant = [&](const u32x4 (&w)[kNB], const uint32_t (&sc)[kNB], int word, f16x8 (&dst)[kNB]) {
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const uint32_t q = word == 0 ? w[nb].x : (word == 1 ? w[nb].y : (word == 2 ? w[nb].z : w[nb].w));
-        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[nb]);
-        dst[nb] = dequant_word_natural(q, f16x2{sv, sv});
-      }
-    };
 
     f32x16 acc[kMB][kNB];
 #pragma unroll
@@ -377,13 +398,8 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 
     const int nsteps = b - a;
     auto clamp = [&](int r) { return a + (r < nsteps ? r : nsteps - 1); };
-    // Prologue: the scale windows of steps 0 and later, steps 0 and 1 into
-    // stages 0 and 1.  (Both window buffers may still be read by the
-    // previous tile until the barrier that ended its last step: passed.)
-    load_window(window_of(a), true);
-    load_window(window_of(a) + 1, true);
-    load_stage(clamp(0), 0);
-    load_stage(clamp(1), 1);
+    // Prologue: the loads of the first windows and steps 0 and 1 were issued
+    // before the previous item's results were written.
     lds_barrier();
     read_a(0, 0, aop[0]);
     read_a(0, 1, aop[1]);
@@ -401,11 +417,11 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
       // The first step of a window (other than the tile's first) loads the
       // next window; the buffer it fills was last read in the step before.
       const bool win_load = r > 0 && window_of(kt) != window_of(kt - 1);
-      load_window(window_of(kt) + 1, win_load);
+      load_window(cur, window_of(kt) + 1, win_load);
 #pragma unroll
       for (int s = 0; s < kSub; ++s) {
         const int g = 2 * U + s;            // sub-step index mod 3 (8 = 2 mod 3)
-        load_part(clamp(r + 2), st_ld, s);
+        load_part(cur, clamp(r + 2), st_ld, s);
         if (s + 2 < kSub) read_a(st_cur, s + 2, aop[(g + 2) % 3]);
         else read_a(st_nxt, s + 2 - kSub, aop[(g + 2) % 3]);
         if (s == 1) {
@@ -452,18 +468,51 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
       if (++r == nsteps) break;
     }
 
+    // the next item's first loads (stages 0 and 1 and the windows are free
+    // once the last step's barrier has passed)
+    if (item + 1 < n_items) {
+      const Item nxt = setup(item + 1);
+      prologue_loads(nxt);
+      cur = nxt;
+    }
+
     if (dp) {
-      // lane holds column li of each block, rows 8*(r/4) + 4*h + r%4
+      // Output through LDS (stage 2, free once the last step's barrier has
+      // passed; the next item's first load into it follows that item's first
+      // barrier): each wave writes its 128 x 64 fp16 slab in two passes of 64
+      // rows into its own 9 KB, [row][64 columns] with a 144-byte row pitch
+      // (every write offset a constant, reads nearly free of bank
+      // conflicts), then stores whole 16-byte chunks, 8 lanes per 128-byte
+      // row.  The accumulator of lane (li, h) holds column li of each block,
+      // rows 8 * (r / 4) + 4 * h + r % 4.
+      constexpr int kPitch = 144;
+      uint8_t* ep = stage2 + wave * 64 * kPitch;
+      uint8_t* ew = ep + 4 * h * kPitch + li * 2;
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const int n = nw + nb * 32 + li;
-        if (n >= N) continue;
+      for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) {
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (m < M) y[(size_t)m * N + n] = float_to_half_bits(acc[i][nb][r]);
+          for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              *reinterpret_cast<uint16_t*>(ew + (ii * 32 + 8 * (r >> 2) + (r & 3)) * kPitch + nb * 64) =
+                  float_to_half_bits(acc[2 * pass + ii][nb][r]);
+        // a wave's LDS accesses complete in order: its own writes are visible
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = 8 * j + (lane >> 3), c = lane & 7;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(ep + row * kPitch + c * 16);
+          const int m = m0 + 64 * pass + row, n = nw + 8 * c;
+          if (m < M) {
+            uint16_t* dst = y + (size_t)m * N + n;
+            if (n + 8 <= N && (N & 7) == 0) {
+              *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
       }
