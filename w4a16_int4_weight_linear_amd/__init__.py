@@ -24,6 +24,15 @@ LIB_PATH = os.path.join(_HERE, "libw4a16.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first (python -m w4a16_int4_weight_linear_amd.build)")
 
+# PyTorch ships its own HIP runtime under the same soname as the system one.
+# Whichever is loaded first serves the whole process, and torch's streams and
+# allocations must come from the runtime the library uses, so torch (when it
+# is installed) is imported before the library is loaded.
+try:
+    import torch as _torch_preload  # noqa: F401
+except ImportError:  # no torch: the host routines (quantise / pack) still work
+    _torch_preload = None
+
 lib = ctypes.CDLL(LIB_PATH)
 
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t

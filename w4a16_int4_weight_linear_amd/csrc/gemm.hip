@@ -660,6 +660,7 @@ hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
               : tail       ? gemm_kernel<32, true, false>
               : salign     ? gemm_kernel<32, false, true>
                            : gemm_kernel<32, false, false>;
+  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
   hipLaunchKernelGGL(kern, dim3(p.wgs), dim3(kThreads), 0, stream, x, packed, scales, y, m, n, k, p.tiles_m,
                      p.tiles_n, p.iters, p.rounds, p.sk_tiles, p.nsk, partials, flags, counters);
   return hipGetLastError();

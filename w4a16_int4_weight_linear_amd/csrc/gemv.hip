@@ -311,6 +311,7 @@ hipError_t launch_gemv_m(const uint16_t* x, const uint32_t* packed, const uint16
   }
   const int gshift = group == 128 ? 2 : 0;   // log2(group / 32)
   const int blocks = (plan.waves_total + kGemvWaves - 1) / kGemvWaves;
+  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
   hipLaunchKernelGGL(gemv_kernel<M>, dim3(blocks), dim3(kGemvThreads), plan.lds, stream, x, packed, scales, y, n,
                      k, gshift, plan.waves_total, plan.rows_base, plan.rows_extra);
   return hipGetLastError();

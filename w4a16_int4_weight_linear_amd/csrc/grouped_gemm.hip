@@ -159,6 +159,7 @@ hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const 
                                int group, const DeviceInfo&, hipStream_t stream) {
   const int tiles_n = (n + BN - 1) / BN;
   const int gshift = group == 128 ? 2 : 0;
+  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
   hipLaunchKernelGGL(grouped_gemm_kernel, dim3(experts * tiles_n), dim3(kThreads), 0, stream, x, packed, scales,
                      offsets, y, n, k, gshift, tiles_n, rows);
   return hipGetLastError();
