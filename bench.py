@@ -45,6 +45,12 @@ def parse():
     ap.add_argument("--components", default="decode,np4,prefill,moe",
                     help="comma list of parts to measure (decode is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch a 256 MiB elementwise copy and the decode GEMV "
+                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes)")
+    ap.add_argument("--traffic-reduce", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the two counter_collection.csv files of the --traffic-probe "
+                         "passes into profiles/gemv.traffic.json (host only, no GPU)")
     return ap.parse_args()
 
 
@@ -249,6 +255,77 @@ def moe_component(torch, w4, synth, args):
             "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, "tflops": fl / (mean * 1e-3) / 1e12}
 
 
+def traffic_probe(torch, w4, synth):
+    """Launch sequence for the HBM counter passes: three plain elementwise copies
+    of a 256 MiB fp16 buffer (known traffic: 256 MiB read + 256 MiB written each),
+    then 8 up- and 8 down-projection decode GEMV launches, each on its own pool
+    copy of the weights.  Prints one line naming the launches."""
+    copy_bytes = 256 << 20
+    src = torch.randn(copy_bytes // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    res = {}
+    for name in ("gemv_up_1x5120x17408_g128", "gemv_down_1x17408x5120_g128"):
+        case = synth.DENSE_CASES[name]
+        w, x = synth.dense_inputs(case)
+        p, s = w4.quantize(w, 128)
+        pool = make_pool(torch, p, s, POOL_BYTES // 2)
+        x_t = torch.from_numpy(x).to("cuda")
+        y = torch.empty((1, case.n), dtype=torch.float16, device="cuda")
+        for i in range(8):
+            pp, ss = pool[i % len(pool)]
+            w4.gemv(x_t, pp, ss, 128, out=y)
+        torch.cuda.synchronize()
+        res[name] = {"algorithmic_bytes": dense_bytes(1, case.n, case.k, 128)}
+        del pool
+    print(json.dumps({"traffic_probe": {"copy_bytes_each_way": copy_bytes, "gemv": res}}))
+
+
+def traffic_reduce(fetch_csv, write_csv):
+    """HBM bytes per decode GEMV launch from the two counter passes.
+
+    FETCH_SIZE and WRITE_SIZE are read per dispatch in KiB and each is scaled by
+    what it reads for the probe's plain elementwise copy, whose true traffic is
+    known (256 MiB read, 256 MiB written); the GEMV's bytes per launch are the
+    scaled fetch plus the scaled write, averaged over its launches."""
+    import csv
+
+    def per_kernel(path):
+        copies, gemv = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                v = float(r["Counter_Value"]) * 1024.0
+                if "neg_kernel" in r["Kernel_Name"]:
+                    copies.append(v)
+                elif "gemv_kernel<1>" in r["Kernel_Name"]:
+                    gemv.append(v)
+        if not copies or not gemv:
+            raise SystemExit(f"{path}: copy or gemv dispatches missing")
+        return float(np.mean(copies)), gemv
+
+    copy_bytes = 256 << 20
+    f_copy, f_gemv = per_kernel(fetch_csv)
+    w_copy, w_gemv = per_kernel(write_csv)
+    f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
+    per_launch = [f * f_scale + w * w_scale for f, w in zip(f_gemv, w_gemv)]
+    rec = {
+        "kernel": "gemv_kernel<1>",
+        "workload": "decode GEMV M=1, up K=5120->N=17408 and down K=17408->N=5120, g128",
+        "source_hash": source_hash("gemv.hip", "device.hpp"),
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "launches": len(per_launch),
+        "bytes_per_launch": int(round(float(np.mean(per_launch)))),
+        "algorithmic_bytes_per_launch": dense_bytes(1, 17408, 5120, 128),
+    }
+    with open(os.path.join(ROOT, "profiles", "gemv.traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def cpu_baseline(decode):
     """The fp64 oracle on the host, over one decode step (up + down), timed."""
     import oracle
@@ -275,6 +352,9 @@ def cpu_baseline(decode):
 
 def main():
     args = parse()
+    if args.traffic_reduce:
+        traffic_reduce(*args.traffic_reduce)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1",
                           "reason": "the W4A16 layer is built and measured on a single MI355X"}))
@@ -286,6 +366,9 @@ def main():
     import synth
     import w4a16_int4_weight_linear_amd as w4
 
+    if args.traffic_probe:
+        traffic_probe(torch, w4, synth)
+        return
     comps = [c for c in args.components.split(",") if c]
     res = {}
     if "decode" not in comps:
