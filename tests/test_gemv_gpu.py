@@ -30,8 +30,10 @@ def run_gemv(w4, x, packed, scales, group):
 
 # (n, k, group): several row counts (1 row, fewer rows than waves, ragged),
 # K giving whole and ragged lane coverage (k/16 = 8, 64, 130, 320, 1088 pieces).
+# The last three cut rows between waves: one 512-chunk row per workgroup shared
+# by 8 or 16 waves, 2-3 rows per workgroup, and 19-20 one-item rows.
 EXACT_SHAPES = [(1, 128, 128), (37, 1024, 32), (300, 5120, 128), (65, 384, 128), (130, 2080, 32),
-                (2049, 2048, 32), (20, 17408, 128)]
+                (2049, 2048, 32), (20, 17408, 128), (256, 16384, 128), (600, 5120, 32), (5000, 1024, 32)]
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4])

@@ -6,21 +6,36 @@
 // GEMVs at the DRAM bandwidth wall, so the kernel streams the packed weights
 // once, at full HBM rate, and keeps the per-byte instruction count low:
 //
-// * Work split: each 64-lane wavefront owns a contiguous run of output rows
-//   (counts differ by at most one across waves); the four waves of a
-//   workgroup own consecutive runs.  For a row, lane l covers the 32-weight
-//   chunks c = l, l+64, l+128, ...: every load is one 16-byte packed chunk per
-//   lane, 1 KiB contiguous per wave.  R rows (1 or 2) are processed together so
-//   each activation read from LDS serves R rows.
+// * Work split: one workgroup per CU, each owning a contiguous block of rows
+//   (block sizes differ by at most one row).  Rows are contiguous in memory, so
+//   the block is one run of bytes; it is cut into 1 KiB items (one 16-byte load
+//   per lane, 64 chunks of 32 weights), and the items are divided evenly among
+//   the workgroup's eight wavefronts regardless of row boundaries.  Every wave
+//   thus reads one sequential stream (which HBM serves faster than interleaved
+//   streams), no lane idles at a row's ragged end, and all waves stream the
+//   same number of bytes.
+// * Lane l of item u holds chunk 64u + l of the block.  The chunk's group
+//   scale index is simply (64u + l) / (g / 32), so the scale address advances
+//   uniformly; the chunk's position in its row (for the activations) advances by
+//   64 and wraps at the row length, one compare per item.  An item that contains
+//   a row end splits its lanes between the two rows (a wave-uniform test); the
+//   finished row is reduced across lanes at once.
+// * Rows cut between waves are finished without a workgroup barrier: each wave
+//   leaves the wave-reduced partial sums of its first and last row in LDS and
+//   bumps the row's counter; the wave that brings the counter to the number of
+//   contributors adds the partials in wave order (deterministic).  Finished rows
+//   collect in LDS and each wave writes its own to y after its loop, so the
+//   loop itself issues no global stores.
 // * The weights come through buffer loads marked non-temporal, issued a fixed
-//   number of chunks ahead of use (a software pipeline over the wave's
-//   flattened (row group, chunk) sequence).  The row offset goes in the scalar
-//   offset field, so a load costs no vector address arithmetic; loads past the
-//   end use an offset outside the buffer and return zero without touching
-//   memory.
+//   number of items ahead of use.  The item offset goes in the scalar offset
+//   field, so a load costs no vector address arithmetic; loads past the end use
+//   an offset outside the buffer and return zero without touching memory.
 // * Once per workgroup, the activations (pre-arranged to line up with the
 //   nibble pairs below), their per-chunk sums and the group scales of the
-//   workgroup's rows are staged in LDS.
+//   workgroup's rows are staged in LDS.  Their global loads are issued before
+//   the first weight loads, so waiting for them does not wait for (and drain)
+//   the weight stream.  In the main loop the LDS reads of the next item are
+//   issued before the current item's arithmetic (M <= 2).
 // * Dequantisation in registers without conversion instructions: masking a
 //   packed word with 0x000F000F leaves the nibbles k = 8j and 8j+4 in the two
 //   fp16 halves as the subnormals u * 2^-24 (exact); 0x00F000F0 leaves
@@ -45,254 +60,364 @@ namespace {
 // Launch shape.  Defaults are the measured best on MI355X; the macros only
 // exist so a sweep can rebuild the library with other values.
 #ifndef W4A16_GEMV_LOADS_IN_FLIGHT
-#define W4A16_GEMV_LOADS_IN_FLIGHT 8
+#define W4A16_GEMV_LOADS_IN_FLIGHT 4
 #endif
-#ifndef W4A16_GEMV_WAVES_PER_CU
-#define W4A16_GEMV_WAVES_PER_CU 8
+#ifndef W4A16_GEMV_THREADS
+#define W4A16_GEMV_THREADS 512
 #endif
-constexpr int kGemvThreads = 512;   // 8 wavefronts per workgroup
+constexpr int kGemvThreads = W4A16_GEMV_THREADS;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kLoadsInFlight = W4A16_GEMV_LOADS_IN_FLIGHT;   // 16-byte loads per lane
-constexpr int kWavesPerCU = W4A16_GEMV_WAVES_PER_CU;
 constexpr uint32_t kScaleSlack = 256;   // staged past the workgroup's last scale
+constexpr int kPartSlots = 4;           // floats per partial slot: M <= 4
 
 template <int M>
 struct XSumSlots { static constexpr int value = (M == 1) ? 1 : (M == 2 ? 2 : 4); };
 
-// Rows processed together: two when the activation reads from LDS would
-// otherwise outrun LDS bandwidth (M >= 3).
-template <int M>
-struct RowsTogether { static constexpr int value = M >= 3 ? 2 : 1; };
-
 struct GemvLayout {
-  uint32_t xs, xsum, sc, total;   // byte offsets of the LDS regions, and the size
+  uint32_t xs, sc, part, cnt, res, total;   // byte offsets of the LDS regions, and the size
 };
 
 __host__ __device__ inline GemvLayout gemv_layout(int m, int chunks, int spr, int rows_wg) {
-  const int xs_slots = m == 1 ? 1 : (m == 2 ? 2 : 4);
-  const uint32_t padded = (uint32_t)((chunks + 63) & ~63);   // whole items of 64 chunks
   GemvLayout l;
   l.xs = 0;
-  l.xsum = padded * (uint32_t)m * 64u;
-  l.sc = l.xsum + padded * (uint32_t)xs_slots * 4u;
-  l.total = l.sc + (((uint32_t)rows_wg * (uint32_t)spr * 2u + 15u) & ~15u) + 32u + kScaleSlack;
+  l.sc = (uint32_t)chunks * (uint32_t)(4 * m + 1) * 16u;
+  l.part = l.sc + (((uint32_t)rows_wg * (uint32_t)spr * 2u + 15u) & ~15u) + 32u + kScaleSlack;
+  l.cnt = l.part + (uint32_t)(kGemvWaves * 2 * kPartSlots * 4);
+  l.res = l.cnt + (((uint32_t)rows_wg * 4u + 15u) & ~15u);
+  l.total = l.res + (uint32_t)rows_wg * (uint32_t)m * 4u;
   return l;
 }
 
-// LDS layout (chunk c = 32 consecutive k of a row; item i = c / 64, lane = c % 64):
-//   xs[i][m][j][lane] : 16 bytes = for word j of chunk c, the fp16 pairs
-//              (x[8j], x[8j+4]), (x[8j+2], x[8j+6]), (x[8j+1], x[8j+5]),
-//              (x[8j+3], x[8j+7]) of activation row m (lanes read consecutive
-//              16-byte slots: no bank conflicts, offsets are immediates);
-//   xsum[c][slot] : -8 * 2^-20 * (sum of the chunk's 32 activations of row slot), fp32;
-//   sc : a 16-byte-aligned copy of the scales of the workgroup's rows (plus slack).
+// s_waitcnt with only the LDS/scalar counter at zero (vector memory and export
+// counters left at their maxima).
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
+
+// LDS layout (chunk c = 32 consecutive k of a row):
+//   xs[c] : (4M + 1) slots of 16 bytes: slot 4m + j = for word j of chunk c the
+//           fp16 pairs (x[8j], x[8j+4]), (x[8j+2], x[8j+6]), (x[8j+1], x[8j+5]),
+//           (x[8j+3], x[8j+7]) of activation row m; slot 4M = -8 * 2^-20 * (sum of
+//           the chunk's 32 activations) for each row.  The chunk stride (an odd
+//           number of 16-byte slots) keeps the 16-byte reads of 16 consecutive
+//           chunks on distinct banks, and one address serves all slots;
+//   sc : a 16-byte-aligned copy of the scales of the workgroup's rows (plus slack);
+//   part[wave][2][4] : partial sums of the first / last row of each wave;
+//   cnt[row] : how many waves have left a partial sum of the row;
+//   res[row][m] : finished fp32 sums, written to y by the wave that finished them.
 template <int M>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
             const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
-            int n, int k, int gshift, int waves_total, int rows_base, int rows_extra) {
+            int n, int k, int gshift, int rows_base, int rows_extra) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int XS = XSumSlots<M>::value;
-  constexpr int R = RowsTogether<M>::value;
-  constexpr int U = kLoadsInFlight / R;          // items (row group, chunk index) in flight
+  constexpr int U = kLoadsInFlight;              // items in flight
+  constexpr uint32_t kChunkBytes = (4 * M + 1) * 16;
+  constexpr uint32_t kSumSlot = 4 * M * 16;
+  // LDS operands of the next item are read ahead while they fit in registers.
+  constexpr bool kReadAhead = M <= 2;
   const int C = k >> 5;                          // 32-weight chunks per row
-  const int IPR = (C + 63) >> 6;                 // chunks per lane per row
   const int spr = C >> gshift;                   // scales per row
-  const bool ragged = (C & 63) != 0;
 
   const int lane = threadIdx.x & 63;
-  // wave index, made explicitly wave-uniform so the row bookkeeping lives in SGPRs
+  // wave index, made explicitly wave-uniform so the bookkeeping lives in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  auto row_start = [&](int w) { return w * rows_base + (w < rows_extra ? w : rows_extra); };
-  const int wg_first = blockIdx.x * kGemvWaves;
-  const int gw = wg_first + wave;
-  const int r0 = row_start(gw);
-  const int nrows = gw < waves_total ? rows_base + (gw < rows_extra ? 1 : 0) : 0;
-  const int wg_r0 = row_start(wg_first);
-  const int wg_last = wg_first + kGemvWaves < waves_total ? wg_first + kGemvWaves : waves_total;
-  const int wg_rows = row_start(wg_last) - wg_r0;
-  const GemvLayout L = gemv_layout(M, C, spr, kGemvWaves * (rows_base + 1));
+  const int blk = blockIdx.x;
+  const int nr = rows_base + (blk < rows_extra ? 1 : 0);                 // rows of this workgroup
+  const int wg_r0 = blk * rows_base + (blk < rows_extra ? blk : rows_extra);
+  const int chunks = nr * C;                                             // chunks of the block
+  const int items = (chunks + 63) >> 6;                                  // 1 KiB items
+  auto bound = [&](int w) { return (int)(((int64_t)w * items) / kGemvWaves); };
+  const int t0 = bound(wave), t1 = bound(wave + 1);                      // this wave's items
+  const GemvLayout L = gemv_layout(M, C, spr, rows_base + (rows_extra ? 1 : 0));
 
-  const int groups = (nrows + R - 1) / R;        // row groups of this wave
-  const int total = groups * IPR;                // items
+  // ---- staging loads (activations, scales), issued before the weight stream ----
+  const uint32_t sc_begin = (uint32_t)wg_r0 * (uint32_t)spr * 2u;
+  const uint32_t sc_a0 = sc_begin & ~15u;
+  const uint32_t sc_chunks = (sc_begin - sc_a0 + (uint32_t)nr * (uint32_t)spr * 2u + kScaleSlack + 15u) >> 4;
+  const uint32_t sc_bytes = (uint32_t)n * (uint32_t)spr * 2u;
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, sc_bytes);
+  const int pairs = C * M;                        // (chunk, activation row) pairs
+  u32x4 a[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = threadIdx.x + h * kGemvThreads;
+    if (idx < pairs) {
+      const int c = idx / M, m = idx - (idx / M) * M;
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)m * k + (size_t)c * 32);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) a[h][w] = src[w];
+    }
+  }
+  const u32x4 sv = load16_tail(sres, threadIdx.x < sc_chunks ? sc_a0 + threadIdx.x * 16u : kOutOfRange, sc_bytes);
 
+  // ---- weight stream: items t0 .. t1-1 of this wave ----
   const uint32_t row_bytes = (uint32_t)k >> 1;
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed, (uint32_t)n * row_bytes);
+  const int rem = chunks - ((items - 1) << 6);   // live lanes of the block's last item
   const uint32_t voff_full = (uint32_t)lane * 16u;
-  const bool lane_live_last = !ragged || (lane + ((IPR - 1) << 6)) < C;
-  const uint32_t voff_last = lane_live_last ? voff_full : kOutOfRange;
-
-  u32x4 wb[U][R];
-  int iss_g = 0, iss_i = 0;
+  const uint32_t voff_end = lane < rem ? voff_full : kOutOfRange;
+  u32x4 wb[U];
+  int iss = t0;
+  uint32_t iss_off = (uint32_t)wg_r0 * row_bytes + ((uint32_t)t0 << 10);
   auto issue = [&](int slot) {
-    const uint32_t voff = (iss_i == IPR - 1) ? voff_last : voff_full;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int rl = iss_g * R + j;
-      const uint32_t soff = (iss_g < groups && rl < nrows)
-                                ? (uint32_t)(r0 + rl) * row_bytes + ((uint32_t)iss_i << 10)
-                                : kOutOfRange;
-      wb[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, voff, soff, kStream));
-    }
-    if (++iss_i == IPR) { iss_i = 0; ++iss_g; }
+    const uint32_t voff = iss == items - 1 ? voff_end : voff_full;
+    wb[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        wres, voff, iss < t1 ? iss_off : kOutOfRange, kStream));
+    ++iss;
+    iss_off += 1024u;
   };
-
-  // Start the weight stream before staging, so the latencies overlap.
 #pragma unroll
   for (int u = 0; u < U; ++u) issue(u);
 
-  // Stage the scales of this workgroup's rows: a 16-byte-aligned window of the
-  // scale array, loaded whole (reads past the array return zero).
-  const uint32_t sc_begin = (uint32_t)wg_r0 * (uint32_t)spr * 2u;
-  const uint32_t sc_a0 = sc_begin & ~15u;
-  const uint32_t sc_chunks = (sc_begin - sc_a0 + (uint32_t)wg_rows * (uint32_t)spr * 2u + kScaleSlack + 15u) >> 4;
-  const uint32_t sc_bytes = (uint32_t)n * (uint32_t)spr * 2u;
-  const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, sc_bytes);
-  // Stage x in batches of two (chunk, row slot) pairs per thread, loads first.
-  const int pairs = C * M;
+  // ---- staging: activations regrouped to the nibble pairing, chunk sums, scales ----
   const uint32_t one2 = 0x3C003C00u;  // fp16 pair (1, 1)
-  for (int b0 = threadIdx.x; b0 < pairs || (b0 == (int)threadIdx.x && (uint32_t)threadIdx.x < sc_chunks);
-       b0 += 2 * kGemvThreads) {
-    u32x4 a[2][4];
+  auto stage_pair = [&](int idx, const u32x4 (&v4)[4]) {
+    const int c = idx / M, m = idx - (idx / M) * M;
+    uint8_t* cp = smem + L.xs + (uint32_t)c * kChunkBytes;
+    float s = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int idx = b0 + h * kGemvThreads;
-      if (idx < pairs) {
-        const int c = idx / M, m = idx - (idx / M) * M;
-        const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)m * k + (size_t)c * 32);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) a[h][w] = src[w];
-      }
+    for (int w = 0; w < 4; ++w) {
+      const u32x4 v = v4[w];          // x[32c+8w .. +7] as pairs (0,1),(2,3),(4,5),(6,7)
+      s = dot2(v.x, one2, s);
+      s = dot2(v.y, one2, s);
+      s = dot2(v.z, one2, s);
+      s = dot2(v.w, one2, s);
+      u32x4 p;                        // regrouped to (0,4),(2,6),(1,5),(3,7)
+      p.x = (v.x & 0xFFFFu) | (v.z << 16);
+      p.y = (v.y & 0xFFFFu) | (v.w << 16);
+      p.z = (v.x >> 16) | (v.z & 0xFFFF0000u);
+      p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+      *reinterpret_cast<u32x4*>(cp + (m * 4 + w) * 16) = p;
     }
-    u32x4 sv[2];
-    const bool first = b0 == (int)threadIdx.x;
-    if (first) {
+    float* sum = reinterpret_cast<float*>(cp + kSumSlot);
+    sum[m] = s * -0x1p-17f;   // -8 * 2^-20 * sum
+    if (M == 3 && m == 0) sum[3] = 0.f;
+  };
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t t = threadIdx.x + h * kGemvThreads;
-        sv[h] = load16_tail(sres, t < sc_chunks ? sc_a0 + t * 16u : kOutOfRange, sc_bytes);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int idx = b0 + h * kGemvThreads;
-      if (idx < pairs) {
-        const int c = idx / M, m = idx - (idx / M) * M;
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const u32x4 v = a[h][w];      // x[32c+8w .. +7] as pairs (0,1),(2,3),(4,5),(6,7)
-          s = dot2(v.x, one2, s);
-          s = dot2(v.y, one2, s);
-          s = dot2(v.z, one2, s);
-          s = dot2(v.w, one2, s);
-          u32x4 p;                      // regrouped to (0,4),(2,6),(1,5),(3,7)
-          p.x = (v.x & 0xFFFFu) | (v.z << 16);
-          p.y = (v.y & 0xFFFFu) | (v.w << 16);
-          p.z = (v.x >> 16) | (v.z & 0xFFFF0000u);
-          p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-          const uint32_t off = (uint32_t)((((c >> 6) * M + m) * 4 + w) * 1024 + (c & 63) * 16);
-          *reinterpret_cast<u32x4*>(smem + L.xs + off) = p;
-        }
-        reinterpret_cast<float*>(smem + L.xsum)[c * XS + m] = s * -0x1p-17f;   // -8 * 2^-20 * sum
-      }
-    }
-    if (first) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t t = threadIdx.x + h * kGemvThreads;
-        if (t < sc_chunks) *reinterpret_cast<u32x4*>(smem + L.sc + t * 16u) = sv[h];
-      }
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int idx = threadIdx.x + h * kGemvThreads;
+    if (idx < pairs) stage_pair(idx, a[h]);
   }
-  for (uint32_t t = threadIdx.x + 2 * kGemvThreads; t < sc_chunks; t += kGemvThreads) {
+  if (threadIdx.x < sc_chunks) *reinterpret_cast<u32x4*>(smem + L.sc + threadIdx.x * 16u) = sv;
+  // Wide activations (more than two pairs per thread) and long scale windows.
+  for (int idx = threadIdx.x + 2 * kGemvThreads; idx < pairs; idx += kGemvThreads) {
+    const int c = idx / M, m = idx - (idx / M) * M;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)m * k + (size_t)c * 32);
+    u32x4 v4[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v4[w] = src[w];
+    stage_pair(idx, v4);
+  }
+  for (uint32_t t = threadIdx.x + kGemvThreads; t < sc_chunks; t += kGemvThreads) {
     *reinterpret_cast<u32x4*>(smem + L.sc + t * 16u) = load16_tail(sres, sc_a0 + t * 16u, sc_bytes);
   }
-  if (M == 3) {
-    for (int c = threadIdx.x; c < C; c += kGemvThreads) reinterpret_cast<float*>(smem + L.xsum)[c * XS + 3] = 0.f;
-  }
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + L.cnt);
+  for (int r = threadIdx.x; r < nr; r += kGemvThreads) cnt[r] = 0u;
   __syncthreads();
 
-  float acc[R][M];
+  // ---- main loop over this wave's items ----
+  float* parts = reinterpret_cast<float*>(smem + L.part);
+  float* res = reinterpret_cast<float*>(smem + L.res);
+  // Lane's chunk in the block: f = 64 t + lane; its chunk in the row, c = f mod C,
+  // addresses the activations; f >> gshift indexes the block's scales.
+  const int f_first = (t0 << 6) + lane;
+  const uint32_t xs_end = L.xs + (uint32_t)C * kChunkBytes;
+  const uint32_t xs_wrap = (uint32_t)C * kChunkBytes;
+  const uint32_t x_step = 64u * kChunkBytes;   // advance by 64 chunks (C >= 64: one wrap at most)
+  // For rows shorter than 64 chunks the step is 64 mod C chunks (whole rows skipped).
+  const uint32_t x_adv = C >= 64 ? x_step : (uint32_t)(64 % C) * kChunkBytes;
+  const uint32_t sc_base = L.sc + (sc_begin - sc_a0);
+  const uint32_t s_step = (uint32_t)((64 >> gshift) * 2);
+  struct Pos {
+    uint32_t xa, sa;   // LDS addresses of the lane's activations and scale
+  };
+  auto advance = [&](Pos& p) {
+    const uint32_t nx = p.xa + x_adv;
+    p.xa = nx >= xs_end ? nx - xs_wrap : nx;
+    p.sa += s_step;
+  };
+  struct Opnd {
+    u32x4 xv[M][4];
+    float xsv[XS];
+    uint32_t s;
+  };
+  auto read_opnd = [&](const Pos& p, Opnd& o) {
+    const uint8_t* xp = smem + p.xa;
 #pragma unroll
-  for (int j = 0; j < R; ++j)
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[j][m] = 0.f;
+      for (int w = 0; w < 4; ++w) o.xv[m][w] = *reinterpret_cast<const u32x4*>(xp + (m * 4 + w) * 16);
+    const uint8_t* sp = xp + kSumSlot;
+    if constexpr (XS == 1) {
+      o.xsv[0] = *reinterpret_cast<const float*>(sp);
+    } else if constexpr (XS == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(sp);
+      o.xsv[0] = v.x; o.xsv[1] = v.y;
+    } else {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sp);
+      o.xsv[0] = v.x; o.xsv[1] = v.y; o.xsv[2] = v.z; o.xsv[3] = v.w;
+    }
+    o.s = *reinterpret_cast<const uint16_t*>(smem + p.sa);
+  };
 
-  const uint32_t xs_lane = L.xs + (uint32_t)lane * 16u;
-  const uint32_t xsum_lane = L.xsum + (uint32_t)lane * (uint32_t)(XS * 4);
-  const uint32_t sc_lane = L.sc + (sc_begin - sc_a0) + ((uint32_t)lane >> gshift) * 2u;
-  int con_g = 0, con_i = 0;
+  // One chunk: s * 2^-20 * sum x (u - 8) for each activation row.
+  auto chunk_dot = [&](const u32x4& q4, const Opnd& o, float (&v)[M]) {
+    float lo[M], hi[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) { lo[m] = 0.f; hi[m] = o.xsv[m]; }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t q = w == 0 ? q4.x : (w == 1 ? q4.y : (w == 2 ? q4.z : q4.w));
+      const uint32_t q8 = q >> 8;
+      const uint32_t a0 = q & 0x000F000Fu, b0 = q8 & 0x000F000Fu;
+      const uint32_t c0 = q & 0x00F000F0u, d0 = q8 & 0x00F000F0u;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        lo[m] = dot2(o.xv[m][w].x, a0, lo[m]);
+        lo[m] = dot2(o.xv[m][w].y, b0, lo[m]);
+        hi[m] = dot2(o.xv[m][w].z, c0, hi[m]);
+        hi[m] = dot2(o.xv[m][w].w, d0, hi[m]);
+      }
+    }
+    const float s = half_bits_to_float(o.s);
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[m] = s * __builtin_fmaf(lo[m], 16.f, hi[m]);
+  };
 
-  for (int base = 0; base < total; base += U) {
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+
+  const int r_first = (t0 << 6) / C;             // row of the wave's first chunk
+  int row = r_first;                             // row of lane 0's chunk
+  int row_end = (row + 1) * C;                   // block chunk where that row ends
+  bool comb_first = false, comb_last = false;    // this wave finished a cut row
+
+  // A row's sums for this wave are complete: store them, or leave them as a
+  // partial and let the row's last contributor add all partials.
+  auto finish_row = [&](int r, const float (&tot)[M]) {
+    const bool whole = r * C >= (t0 << 6) && (r + 1) * C <= (t1 << 6);
+    if (whole) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        if (lane == m) res[r * M + m] = tot[m];
+      return;
+    }
+    float* slot = parts + wave * (2 * kPartSlots) + (r == r_first ? 0 : kPartSlots);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (lane == m) slot[m] = tot[m];
+    // LDS accesses of one wave complete in order, so the slot writes land before
+    // the count; the empty asm statements keep the compiler from moving LDS
+    // accesses across the count (a fence would also wait for the weight loads
+    // in flight).
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    uint32_t before = 0;
+    if (lane == 0) before = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    asm volatile("" ::: "memory");
+    const int start = r * C, end = start + C;
+    int contributors = 0;
+    for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+      const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
+      contributors += (a1 > a0 && a0 < end && a1 > start) ? 1 : 0;
+    }
+    if ((int)before == contributors - 1) {
+      if (lane < M) {
+        float sum = 0.f;
+        for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+          const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
+          if (a1 > a0 && a0 < end && a1 > start)
+            sum += parts[w2 * (2 * kPartSlots) + (a0 / C == r ? 0 : kPartSlots) + lane];
+        }
+        res[r * M + lane] = sum;
+      }
+      if (r == r_first) comb_first = true; else comb_last = true;
+    }
+  };
+
+  const int cnt_items = t1 - t0;
+  Pos cur_pos;
+  {
+    const int c0 = f_first % C;
+    cur_pos.xa = L.xs + (uint32_t)c0 * kChunkBytes;
+    cur_pos.sa = sc_base + (uint32_t)(f_first >> gshift) * 2u;
+  }
+  Opnd cur;
+  if (kReadAhead && cnt_items > 0) read_opnd(cur_pos, cur);
+
+  // One item: u is its load slot, idx its index among this wave's items.
+  auto consume = [&](int u, int idx) {
+    Pos nxt = cur_pos;
+    advance(nxt);
+    Opnd on;
+    if constexpr (kReadAhead) {
+      if (idx + 1 < cnt_items) read_opnd(nxt, on);
+    } else {
+      read_opnd(cur_pos, cur);
+    }
+    float v[M];
+    chunk_dot(wb[u], cur, v);
+    const int f0 = (t0 + idx) << 6;              // block chunk of lane 0
+    if (row_end <= f0 + 64) {
+      // One or more rows end inside this item: lanes before each end finish that row.
+      do {
+        const int b = row_end - f0;              // lanes [0, b) belong to rows up to `row`
+        float tot[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float mine = lane < b ? v[m] : 0.f;
+          v[m] -= mine;
+          tot[m] = wave_sum(acc[m] + mine) * 0x1p20f;
+          acc[m] = 0.f;
+        }
+        if (row < nr) finish_row(row, tot);
+        ++row;
+        row_end += C;
+      } while (row_end <= f0 + 64);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] += v[m];
+    cur_pos = nxt;
+    if constexpr (kReadAhead) cur = on;
+  };
+  int base = 0;
+  for (; base + U <= cnt_items; base += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (base + u < total) {
-        const bool last = con_i == IPR - 1;
-        const bool live = !last || lane_live_last;
-        const uint8_t* xp = smem + xs_lane + (uint32_t)con_i * (uint32_t)(M * 4096);
-        float xsv[XS];
-        {
-          const uint8_t* sp = smem + xsum_lane + ((uint32_t)con_i << 6) * (uint32_t)(XS * 4);
-          if constexpr (XS == 1) {
-            xsv[0] = *reinterpret_cast<const float*>(sp);
-          } else if constexpr (XS == 2) {
-            const float2 v = *reinterpret_cast<const float2*>(sp);
-            xsv[0] = v.x; xsv[1] = v.y;
-          } else {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sp);
-            xsv[0] = v.x; xsv[1] = v.y; xsv[2] = v.z; xsv[3] = v.w;
-          }
-        }
-        u32x4 xv[M][4];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) xv[m][w] = *reinterpret_cast<const u32x4*>(xp + (m * 4 + w) * 1024);
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          const int rl = min(con_g * R + j, nrows - 1);         // row index within the wave
-          const uint32_t sofs = sc_lane + (uint32_t)(r0 + rl - wg_r0) * (uint32_t)spr * 2u
-                                + ((((uint32_t)con_i << 6) >> gshift) << 1);
-          const float s = half_bits_to_float(*reinterpret_cast<const uint16_t*>(smem + sofs));
-          float lo[M], hi[M];
-#pragma unroll
-          for (int m = 0; m < M; ++m) { lo[m] = 0.f; hi[m] = xsv[m]; }
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t q = w == 0 ? wb[u][j].x : (w == 1 ? wb[u][j].y : (w == 2 ? wb[u][j].z : wb[u][j].w));
-            const uint32_t q8 = q >> 8;
-            const uint32_t a = q & 0x000F000Fu, b = q8 & 0x000F000Fu;
-            const uint32_t c = q & 0x00F000F0u, d = q8 & 0x00F000F0u;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              lo[m] = dot2(xv[m][w].x, a, lo[m]);
-              lo[m] = dot2(xv[m][w].y, b, lo[m]);
-              hi[m] = dot2(xv[m][w].z, c, hi[m]);
-              hi[m] = dot2(xv[m][w].w, d, hi[m]);
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const float t = live ? __builtin_fmaf(lo[m], 16.f, hi[m]) : 0.f;   // 2^-20 sum x (u - 8)
-            acc[j][m] = __builtin_fmaf(s, t, acc[j][m]);
-          }
-        }
-        if (last) {
-#pragma unroll
-          for (int j = 0; j < R; ++j) {
-            const int rl = con_g * R + j;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              const float v = wave_sum(acc[j][m]) * 0x1p20f;
-              if (lane == m && rl < nrows) y[(size_t)m * n + r0 + rl] = float_to_half_bits(v);
-              acc[j][m] = 0.f;
-            }
-          }
-        }
-        if (++con_i == IPR) { con_i = 0; ++con_g; }
-      }
+      consume(u, base + u);
       issue(u);
+    }
+  }
+  // The last items of the wave: nothing left to load.
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (base + u < cnt_items) consume(u, base + u);
+  }
+  // A row cut at the end of the wave's range.
+  if (cnt_items > 0 && row < nr && row * C < (t1 << 6)) {
+    float tot[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) tot[m] = wave_sum(acc[m]) * 0x1p20f;
+    finish_row(row, tot);
+  }
+
+  // ---- y for the rows this wave finished: whole rows, and cut rows it combined ----
+  if (cnt_items > 0) {
+    const int c_lo = t0 << 6, c_hi = min(t1 << 6, chunks);
+    const int r_last = (c_hi - 1) / C;
+    const int ra = (c_lo % C == 0) ? r_first : r_first + 1;   // first whole row
+    const int rb = (c_hi % C == 0) ? r_last + 1 : r_last;     // end of whole rows
+    // A combined first row lies just before ra, a combined last row at rb (when
+    // the range lies inside one row, only the first flag can be set).
+    const int p0 = comb_first ? r_first : ra;
+    int p1 = comb_last ? r_last + 1 : rb;
+    if (comb_first && p1 < r_first + 1) p1 = r_first + 1;
+    for (int e = p0 * M + lane; e < p1 * M; e += 64) {
+      const int rl = e / M, m = e - (e / M) * M;
+      y[(size_t)m * n + wg_r0 + rl] = float_to_half_bits(res[e]);
     }
   }
 }
@@ -310,43 +435,42 @@ hipError_t launch_gemv_m(const uint16_t* x, const uint32_t* packed, const uint16
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   const int gshift = group == 128 ? 2 : 0;   // log2(group / 32)
-  const int blocks = (plan.waves_total + kGemvWaves - 1) / kGemvWaves;
   (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL(gemv_kernel<M>, dim3(blocks), dim3(kGemvThreads), plan.lds, stream, x, packed, scales, y, n,
-                     k, gshift, plan.waves_total, plan.rows_base, plan.rows_extra);
+  hipLaunchKernelGGL(gemv_kernel<M>, dim3(plan.blocks), dim3(kGemvThreads), plan.lds, stream, x, packed, scales, y,
+                     n, k, gshift, plan.rows_base, plan.rows_extra);
   return hipGetLastError();
 }
 
-size_t plan_lds(int m, int n, int k, int group, int waves_total) {
+size_t plan_lds(int m, int n, int k, int group, int blocks) {
   const int C = k / 32;
   const int spr = C / (group / 32);
-  const int rows_base = n / waves_total, rows_extra = n % waves_total;
-  return gemv_layout(m, C, spr, kGemvWaves * (rows_base + (rows_extra ? 1 : 0))).total;
+  const int rows_base = n / blocks, rows_extra = n % blocks;
+  return gemv_layout(m, C, spr, rows_base + (rows_extra ? 1 : 0)).total;
 }
 
 }  // namespace
 
 GemvPlan gemv_plan(int m, int n, int k, int group, const DeviceInfo& dev) {
   GemvPlan p;
-  int waves_total = n < dev.num_cu * kWavesPerCU ? n : dev.num_cu * kWavesPerCU;
-  // More waves (fewer rows, so fewer staged scales, each) until the LDS fits.
-  while (waves_total < n && plan_lds(m, n, k, group, waves_total) > dev.max_lds) {
-    waves_total = waves_total * 2 < n ? waves_total * 2 : n;
+  // One workgroup per CU; more (fewer rows, so fewer staged scales, each) until the LDS fits.
+  int blocks = n < dev.num_cu ? n : dev.num_cu;
+  while (blocks < n && plan_lds(m, n, k, group, blocks) > dev.max_lds) {
+    blocks = blocks * 2 < n ? blocks * 2 : n;
   }
-  p.waves_total = waves_total;
-  p.rows_base = n / waves_total;
-  p.rows_extra = n % waves_total;
-  p.lds = plan_lds(m, n, k, group, waves_total);
+  p.blocks = blocks;
+  p.rows_base = n / blocks;
+  p.rows_extra = n % blocks;
+  p.lds = plan_lds(m, n, k, group, blocks);
   p.ok = p.lds <= dev.max_lds;
   return p;
 }
 
 int64_t gemv_max_k(int m, int group, const DeviceInfo& dev) {
-  // Fewest rows a workgroup can be given: one per wave.
+  // Fewest rows a workgroup can be given: one.
   int64_t best = 0;
   for (int64_t k = group; k <= (int64_t)1 << 22; k += group) {
     const int C = (int)(k / 32);
-    if (gemv_layout(m, C, C / (group / 32), kGemvWaves).total > dev.max_lds) break;
+    if (gemv_layout(m, C, C / (group / 32), 1).total > dev.max_lds) break;
     best = k;
   }
   return best;

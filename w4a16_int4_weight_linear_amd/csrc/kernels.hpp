@@ -21,7 +21,7 @@ hipError_t current_device_info(DeviceInfo* out);
 
 // ---- decode GEMV (gemv.hip) ----
 struct GemvPlan {
-  int waves_total = 0, rows_base = 0, rows_extra = 0;
+  int blocks = 0, rows_base = 0, rows_extra = 0;   // workgroups; rows per workgroup (+1 for the first rows_extra)
   size_t lds = 0;     // bytes of LDS per workgroup
   bool ok = false;    // false: the activations and scales do not fit in LDS
 };
