@@ -292,49 +292,61 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   const int r_first = (t0 << 6) / C;             // row of the wave's first chunk
   int row = r_first;                             // row of lane 0's chunk
   int row_end = (row + 1) * C;                   // block chunk where that row ends
-  bool comb_first = false, comb_last = false;    // this wave finished a cut row
 
-  // A row's sums for this wave are complete: store them, or leave them as a
-  // partial and let the row's last contributor add all partials.
-  auto finish_row = [&](int r, const float (&tot)[M]) {
-    const bool whole = r * C >= (t0 << 6) && (r + 1) * C <= (t1 << 6);
-    if (whole) {
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        if (lane == m) res[r * M + m] = tot[m];
-      return;
-    }
-    float* slot = parts + wave * (2 * kPartSlots) + (r == r_first ? 0 : kPartSlots);
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if (lane == m) slot[m] = tot[m];
-    // LDS accesses of one wave complete in order, so the slot writes land before
-    // the count; the empty asm statements keep the compiler from moving LDS
-    // accesses across the count (a fence would also wait for the weight loads
-    // in flight).
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    uint32_t before = 0;
-    if (lane == 0) before = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    before = __builtin_amdgcn_readfirstlane(before);
-    asm volatile("" ::: "memory");
-    const int start = r * C, end = start + C;
-    int contributors = 0;
-    for (int w2 = 0; w2 < kGemvWaves; ++w2) {
-      const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
-      contributors += (a1 > a0 && a0 < end && a1 > start) ? 1 : 0;
-    }
-    if ((int)before == contributors - 1) {
-      if (lane < M) {
-        float sum = 0.f;
-        for (int w2 = 0; w2 < kGemvWaves; ++w2) {
-          const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
-          if (a1 > a0 && a0 < end && a1 > start)
-            sum += parts[w2 * (2 * kPartSlots) + (a0 / C == r ? 0 : kPartSlots) + lane];
-        }
-        res[r * M + lane] = sum;
+  // Finished per-lane row sums wait in a queue of four values (rows in order,
+  // M values each) and are reduced across lanes four at a time: a 32-lane and a
+  // 16-lane swap put the four values in the four 16-lane rows, four DPP steps
+  // finish the sums.  Rows the wave holds whole go to res; cut rows to the
+  // wave's partial slots.
+  float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;  // q3 oldest
+  // The lane swaps are written as inline assembly because both registers are
+  // outputs (the compiler's builtins for them lose one of the two results).
+  // The s_nop before and after give the required wait states around them.
+  auto swap32 = [](float& lo, float& hi) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+  };
+  auto swap16 = [](float& lo, float& hi) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+  };
+  int q_row = r_first;                           // row of the oldest queued value
+  int q_n = 0;                                   // values queued
+  const int v_idx = (lane >> 5) | ((lane >> 3) & 2);   // value a lane ends up holding
+  auto flush = [&]() {
+    float a2 = q3, b2 = q2, c2 = q1, d2 = q0;
+    swap32(a2, b2);                              // a2 = a[0:32] | b[0:32], b2 = a[32:64] | b[32:64]
+    swap32(c2, d2);
+    float s1 = a2 + b2, s2 = c2 + d2;            // a | b and c | d, 32 lanes each
+    swap16(s1, s2);                              // 16-lane rows: s1 = a b a b halves, s2 = c d c d
+    float t = s1 + s2;                           // 16-lane rows hold a, c, b, d
+    t = dpp_add<0xB1>(t);    // quad_perm [1,0,3,2]
+    t = dpp_add<0x4E>(t);    // quad_perm [2,3,0,1]
+    t = dpp_add<0x124>(t);   // row_ror:4
+    t = dpp_add<0x128>(t);   // row_ror:8
+    const int r = q_row + v_idx / M, m = v_idx - (v_idx / M) * M;
+    // (rows past the block come from lanes past its end and are dropped)
+    if ((lane & 15) == 0 && v_idx < q_n && r < nr) {
+      const bool whole = r * C >= (t0 << 6) && (r + 1) * C <= (t1 << 6);
+      const float tot = t * 0x1p20f;
+      if (whole) {
+        res[r * M + m] = tot;
+      } else {
+        parts[wave * (2 * kPartSlots) + (r == r_first ? 0 : kPartSlots) + m] = tot;
       }
-      if (r == r_first) comb_first = true; else comb_last = true;
+    }
+    q0 = q1 = q2 = q3 = 0.f;
+    q_row += 4 / M;
+    q_n = 0;
+  };
+  auto push_row = [&](const float (&val)[M]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      q3 = q2; q2 = q1; q1 = q0; q0 = val[m];
+    }
+    q_n += M;
+    if (q_n + M > 4) {
+      // Line the queued values up as q3 = first (M = 3 leaves one empty slot).
+      if (q_n == 3) { q3 = q2; q2 = q1; q1 = q0; q0 = 0.f; }
+      flush();
     }
   };
 
@@ -365,15 +377,15 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
       // One or more rows end inside this item: lanes before each end finish that row.
       do {
         const int b = row_end - f0;              // lanes [0, b) belong to rows up to `row`
-        float tot[M];
+        float fin[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           const float mine = lane < b ? v[m] : 0.f;
           v[m] -= mine;
-          tot[m] = wave_sum(acc[m] + mine) * 0x1p20f;
+          fin[m] = acc[m] + mine;
           acc[m] = 0.f;
         }
-        if (row < nr) finish_row(row, tot);
+        push_row(fin);
         ++row;
         row_end += C;
       } while (row_end <= f0 + 64);
@@ -396,12 +408,55 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   for (int u = 0; u < U; ++u) {
     if (base + u < cnt_items) consume(u, base + u);
   }
-  // A row cut at the end of the wave's range.
-  if (cnt_items > 0 && row < nr && row * C < (t1 << 6)) {
-    float tot[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) tot[m] = wave_sum(acc[m]) * 0x1p20f;
-    finish_row(row, tot);
+  // A row cut at the end of the wave's range, then whatever is still queued.
+  if (cnt_items > 0 && row < nr && row * C < (t1 << 6)) push_row(acc);
+  if (q_n > 0) {
+    if (M == 1) {
+      // Line the queued values up as q3 = first.
+      for (int i = q_n; i < 4; ++i) { q3 = q2; q2 = q1; q1 = q0; q0 = 0.f; }
+    } else if (M == 2 && q_n == 2) {
+      q3 = q1; q2 = q0; q1 = 0.f; q0 = 0.f;
+    }
+    flush();
+  }
+
+  // ---- rows cut between waves: count this wave in; the last contributor adds the partials ----
+  bool comb_first = false, comb_last = false;    // this wave finished a cut row
+  auto count_in = [&](int r) {
+    // LDS accesses of one wave complete in order, so the partial-slot writes land
+    // before the count; the empty asm statements keep the compiler from moving
+    // LDS accesses across the count.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    uint32_t before = 0;
+    if (lane == 0) before = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    asm volatile("" ::: "memory");
+    const int start = r * C, end = start + C;
+    int contributors = 0;
+    for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+      const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
+      contributors += (a1 > a0 && a0 < end && a1 > start) ? 1 : 0;
+    }
+    if ((int)before != contributors - 1) return false;
+    if (lane < M) {
+      float sum = 0.f;
+      for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+        const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
+        if (a1 > a0 && a0 < end && a1 > start)
+          sum += parts[w2 * (2 * kPartSlots) + (a0 / C == r ? 0 : kPartSlots) + lane];
+      }
+      res[r * M + lane] = sum;
+    }
+    return true;
+  };
+  if (cnt_items > 0) {
+    const int c_lo = t0 << 6, c_hi_w = t1 << 6;
+    const int r_last_w = (min(c_hi_w, chunks) - 1) / C;
+    const bool first_cut = !(r_first * C >= c_lo && (r_first + 1) * C <= c_hi_w);
+    const bool last_cut = r_last_w != r_first && !((r_last_w + 1) * C <= c_hi_w);
+    if (first_cut) comb_first = count_in(r_first);
+    if (last_cut) comb_last = count_in(r_last_w);
   }
 
   // ---- y for the rows this wave finished: whole rows, and cut rows it combined ----
