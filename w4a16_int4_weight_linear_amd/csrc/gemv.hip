@@ -68,6 +68,10 @@ namespace {
 constexpr int kGemvThreads = W4A16_GEMV_THREADS;
 constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kLoadsInFlight = W4A16_GEMV_LOADS_IN_FLIGHT;   // 16-byte loads per lane
+#ifndef W4A16_GEMV_SKEW
+#define W4A16_GEMV_SKEW 100
+#endif
+constexpr int kGemvSkew = W4A16_GEMV_SKEW;   // in 1/1024
 constexpr uint32_t kScaleSlack = 256;   // staged past the workgroup's last scale
 constexpr int kPartSlots = 4;           // floats per partial slot: M <= 4
 
@@ -127,7 +131,14 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   const int wg_r0 = blk * rows_base + (blk < rows_extra ? blk : rows_extra);
   const int chunks = nr * C;                                             // chunks of the block
   const int items = (chunks + 63) >> 6;                                  // 1 KiB items
-  auto bound = [&](int w) { return (int)(((int64_t)w * items) / kGemvWaves); };
+  // Waves 0..W/2-1 are the older wave of their SIMD and are issued first, so
+  // they get a larger share (1 + skew) of the items than the younger half.
+  auto bound = [&](int w) {
+    constexpr int kHalf = kGemvWaves / 2;
+    const uint32_t cum = w <= kHalf ? (uint32_t)w * (1024 + kGemvSkew)
+                                    : (uint32_t)kHalf * (1024 + kGemvSkew) + (uint32_t)(w - kHalf) * (1024 - kGemvSkew);
+    return (int)((cum * (uint32_t)items) / (uint32_t)(kGemvWaves * 1024));
+  };
   const int t0 = bound(wave), t1 = bound(wave + 1);                      // this wave's items
   const GemvLayout L = gemv_layout(M, C, spr, rows_base + (rows_extra ? 1 : 0));
 
@@ -153,15 +164,15 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 
   // ---- weight stream: items t0 .. t1-1 of this wave ----
   const uint32_t row_bytes = (uint32_t)k >> 1;
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed, (uint32_t)n * row_bytes);
-  const int rem = chunks - ((items - 1) << 6);   // live lanes of the block's last item
-  const uint32_t voff_full = (uint32_t)lane * 16u;
-  const uint32_t voff_end = lane < rem ? voff_full : kOutOfRange;
+  // The descriptor covers exactly the workgroup's rows, so lanes past the block's
+  // end in its last item read zero without a per-lane offset.
+  const __amdgpu_buffer_rsrc_t wres =
+      make_rsrc(reinterpret_cast<const uint8_t*>(packed) + (size_t)wg_r0 * row_bytes, (uint32_t)nr * row_bytes);
+  const uint32_t voff = (uint32_t)lane * 16u;
   u32x4 wb[U];
   int iss = t0;
-  uint32_t iss_off = (uint32_t)wg_r0 * row_bytes + ((uint32_t)t0 << 10);
+  uint32_t iss_off = (uint32_t)t0 << 10;
   auto issue = [&](int slot) {
-    const uint32_t voff = iss == items - 1 ? voff_end : voff_full;
     wb[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
         wres, voff, iss < t1 ? iss_off : kOutOfRange, kStream));
     ++iss;
@@ -261,7 +272,7 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     o.s = *reinterpret_cast<const uint16_t*>(smem + p.sa);
   };
 
-  // One chunk: s * 2^-20 * sum x (u - 8) for each activation row.
+  // One chunk: 2^-20 * sum x (u - 8) for each activation row (the scale is applied by the caller).
   auto chunk_dot = [&](const u32x4& q4, const Opnd& o, float (&v)[M]) {
     float lo[M], hi[M];
 #pragma unroll
@@ -280,9 +291,8 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
         hi[m] = dot2(o.xv[m][w].w, d0, hi[m]);
       }
     }
-    const float s = half_bits_to_float(o.s);
 #pragma unroll
-    for (int m = 0; m < M; ++m) v[m] = s * __builtin_fmaf(lo[m], 16.f, hi[m]);
+    for (int m = 0; m < M; ++m) v[m] = __builtin_fmaf(lo[m], 16.f, hi[m]);
   };
 
   float acc[M];
@@ -372,9 +382,15 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     }
     float v[M];
     chunk_dot(wb[u], cur, v);
+    const float sc = half_bits_to_float(cur.s);
     const int f0 = (t0 + idx) << 6;              // block chunk of lane 0
-    if (row_end <= f0 + 64) {
+    if (row_end > f0 + 64) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(sc, v[m], acc[m]);
+    } else {
       // One or more rows end inside this item: lanes before each end finish that row.
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[m] *= sc;
       do {
         const int b = row_end - f0;              // lanes [0, b) belong to rows up to `row`
         float fin[M];
@@ -389,9 +405,9 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
         ++row;
         row_end += C;
       } while (row_end <= f0 + 64);
-    }
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] += v[m];
+      for (int m = 0; m < M; ++m) acc[m] += v[m];
+    }
     cur_pos = nxt;
     if constexpr (kReadAhead) cur = on;
   };
@@ -434,6 +450,7 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     asm volatile("" ::: "memory");
     const int start = r * C, end = start + C;
     int contributors = 0;
+#pragma unroll
     for (int w2 = 0; w2 < kGemvWaves; ++w2) {
       const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
       contributors += (a1 > a0 && a0 < end && a1 > start) ? 1 : 0;
@@ -441,7 +458,8 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     if ((int)before != contributors - 1) return false;
     if (lane < M) {
       float sum = 0.f;
-      for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+  #pragma unroll
+    for (int w2 = 0; w2 < kGemvWaves; ++w2) {
         const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
         if (a1 > a0 && a0 < end && a1 > start)
           sum += parts[w2 * (2 * kPartSlots) + (a0 / C == r ? 0 : kPartSlots) + lane];
