@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--traffic-reduce", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the two counter_collection.csv files of the --traffic-probe "
                          "passes into profiles/gemv.traffic.json (host only, no GPU)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "COMMAND"),
+                    help="turn a rocprofv3 kernel trace of this benchmark into the per-kernel "
+                         "summaries profiles/*.kernel_trace.md (host only, no GPU)")
     return ap.parse_args()
 
 
@@ -326,6 +329,65 @@ def traffic_reduce(fetch_csv, write_csv):
     print(json.dumps(rec))
 
 
+def trace_summary(trace_csv, command):
+    """Per-kernel launch statistics of a rocprofv3 kernel trace of bench.py.
+
+    Launches of one kernel with the same grid are split into the benchmark's
+    workloads at the largest gaps between their durations (the workloads of a
+    kernel differ in size: M = 512 / 4096 prefill, N = 5120 / 17408 np4)."""
+    import csv
+    import statistics
+    from collections import defaultdict
+    labels = {"gemm_kernel": ["M=512", "M=4096"],
+              "gemv_kernel<1>": ["one of up 5120->17408 / down 17408->5120 (same bytes)"],
+              "gemv_kernel<4>": ["N=5120", "N=17408"],
+              "grouped_gemm_kernel": ["256 experts, 4096 routed rows, N=512, K=2048, g32"]}
+    files = {"gemv_kernel<1>": "gemv_m1_decode_27b_ffn", "gemv_kernel<4>": "gemv_m4_np4_27b_ffn",
+             "gemm_kernel": "gemm_prefill_27b_ffn", "grouped_gemm_kernel": "grouped_gemm_moe_256e"}
+    groups = defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "w4a16" not in name:
+                continue
+            short = name.replace("w4a16::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            key = (short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]),
+                   int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]))
+            groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+
+    def clusters(d, n):
+        d = sorted(d)
+        if n <= 1 or len(d) < 2:
+            return [d]
+        gaps = sorted(range(1, len(d)), key=lambda i: d[i] - d[i - 1], reverse=True)[: n - 1]
+        cuts = [0] + sorted(gaps) + [len(d)]
+        return [d[cuts[i]:cuts[i + 1]] for i in range(len(cuts) - 1)]
+
+    out = defaultdict(list)
+    for (k, grid, wg, lds, vgpr, agpr), d in sorted(groups.items()):
+        base = "gemm_kernel" if k.startswith("gemm_kernel") else k
+        if base not in files:
+            continue
+        lab = labels[base]
+        for name, c in zip(lab, clusters(d, len(lab))):
+            out[base].append((k, name, grid, wg, lds, vgpr, agpr, len(c), statistics.mean(c),
+                              statistics.median(c), min(c), max(c)))
+    for base, lst in out.items():
+        path = os.path.join(ROOT, "profiles", f"{files[base]}.kernel_trace.md")
+        with open(path, "w") as f:
+            f.write(f"# {base}: rocprofv3 kernel trace of bench.py\n\n")
+            f.write("Command (from the repository root on the GPU box), then the summary:\n\n```\n"
+                    f"{command}\npython3 bench.py --trace-summary <trace dir>/bench_kernel_trace.csv '<command>'\n```\n\n")
+            f.write("Launches of one kernel with the same grid are split into workloads at the largest gaps "
+                    "between their durations.\n\n")
+            f.write("| kernel | workload | grid (threads) | workgroup | LDS bytes | VGPR | AGPR | launches | "
+                    "mean us | median us | min us | max us |\n|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+            for k, name, grid, wg, lds, vgpr, agpr, n, mean, med, mn, mx in lst:
+                f.write(f"| {k} | {name} | {grid} | {wg} | {lds} | {vgpr} | {agpr} | {n} | {mean:.2f} | "
+                        f"{med:.2f} | {mn:.2f} | {mx:.2f} |\n")
+        print("wrote", path)
+
+
 def cpu_baseline(decode):
     """The fp64 oracle on the host, over one decode step (up + down), timed."""
     import oracle
@@ -354,6 +416,9 @@ def main():
     args = parse()
     if args.traffic_reduce:
         traffic_reduce(*args.traffic_reduce)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1",
