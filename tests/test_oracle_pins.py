@@ -427,3 +427,16 @@ def test_pins_catch_planted_mistakes(name):
         except (AssertionError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+def test_manifest_matches():
+    """tests/manifest.json records the seeds, shapes and parity bars actually in use."""
+    import importlib.util
+    import json
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("write_manifest", os.path.join(here, "write_manifest.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with open(os.path.join(here, "manifest.json")) as f:
+        assert json.load(f) == json.loads(json.dumps(mod.manifest()))
