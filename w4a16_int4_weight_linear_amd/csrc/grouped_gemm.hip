@@ -5,151 +5,361 @@
 // the rows offsets[e] .. offsets[e+1]-1 are multiplied by expert e's packed
 // weights.  With a few rows per expert (16 on average for 512 tokens routed
 // top-8 over 256 experts) the work is bound by streaming the experts' weights
-// from HBM, not by the matrix cores, so the kernel is organised around the
-// weight stream:
+// from HBM, not by the matrix cores, so the kernel is organised around that
+// stream:
 //
-// * One 512-thread workgroup per (expert, band of 256 output columns); each
-//   of its eight wavefronts owns 32 columns (two 16-column MFMA blocks).  An
-//   expert that received no rows is skipped without reading its weights.
-// * Each lane streams 16-byte packed chunks (32 consecutive k of one column,
-//   one group of 32 or a quarter of a group of 128, so one scale per chunk)
-//   a few K chunks ahead of use, and dequantises them in registers exactly as
-//   the dense GEMM does (nibble -> fp16 code -> times the group scale).
-// * The expert's activation rows are staged through LDS in K chunks of 128,
-//   32 rows at a time (two 16-row MFMA blocks, v_mfma_f32_16x16x32_f16); more
-//   rows loop over further 32-row passes.
-// * Row offsets are read on the device, so the host never synchronises.
+// * Work items are (expert, block of up to 32 of its rows), found on the device
+//   from the offsets: expert e contributes ceil(rows_e / 32) items, so an
+//   expert that received no rows reads nothing and a heavily routed expert is
+//   spread over many workgroups (which then share its weights through L2/MALL)
+//   instead of looping over its rows in one.
+// * One 512-thread workgroup per (item, band of 256 output columns); each of
+//   its eight waves owns 32 columns (two 16-column MFMA blocks).  The two bands
+//   of an item are placed on the same XCD, so their activation rows meet in one
+//   L2.
+// * Each lane streams 16-byte packed chunks (32 consecutive k of one column) one
+//   K step (4 chunks, 512 k) ahead of use and dequantises them in registers;
+//   the group scales arrive by one vector load per step and block.
+// * The item's activation rows are staged in LDS 512 k at a time, double
+//   buffered, with one workgroup barrier per K step; the next step's rows are
+//   loaded into registers a full step before they are written.
+// * The weights are the MFMA's A operand (v_mfma_f32_16x16x32_f16, 16 columns
+//   x 32 k) and the activations its B operand, so a lane ends with four
+//   consecutive output columns of one row: 8-byte stores.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "mfma_operands.hpp"
+
+#include <type_traits>
 
 namespace w4a16 {
 namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int BN = 256;                 // output columns per workgroup
-constexpr int kWaveN = BN / kWaves;     // 32 columns per wave
-constexpr int kNB = kWaveN / 16;        // 16-column MFMA blocks per wave
-constexpr int BMP = 32;                 // rows per pass
-constexpr int kMB = BMP / 16;
-constexpr int KC = 128;                 // k per chunk
-constexpr int kAPitch = KC * 2 + 16;    // bytes per LDS row (padded)
-constexpr int kATile = BMP * kAPitch;
-constexpr int kDepth = 4;               // weight chunks in flight
+constexpr int BN = 256;                    // output columns per workgroup
+constexpr int kWaveN = 32;                 // columns per wave
+constexpr int kNB = kWaveN / 16;           // 16-column MFMA blocks per wave
+constexpr int RB = 32;                     // rows per work item
+constexpr int KC = 128;                    // k per chunk: 16 bytes per lane and block in operand layout
+constexpr int KS = 2 * KC;                 // k per K step: one 128-byte line per weight row
+constexpr int kDepth = 2;                  // K steps of weights in flight
+constexpr int kAPitch = KS * 2 + 16;       // bytes per staged activation row: rows shift by 4 banks
+constexpr int kABuf = RB * kAPitch;        // one staged activation block
+constexpr int kXPieces = RB * KS / 8 / kThreads;   // 16-byte activation pieces per thread and step
+constexpr int kTileWave = kNB * 16 * 128;  // per-wave weight transpose tile
+constexpr int kTileBase = 2 * kABuf;
+constexpr int kLds = kTileBase + kWaves * kTileWave;
 
-__global__ void __launch_bounds__(kThreads)
-grouped_gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
-                    const uint16_t* __restrict__ scales, const int32_t* __restrict__ offsets,
-                    uint16_t* __restrict__ y, int N, int K, int gshift, int tiles_n, int rows_total) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2 * kATile];
+static_assert(kXPieces == 2, "activation staging assumes two pieces per thread");
+static_assert(kLds <= 80 * 1024, "two workgroups per CU");
 
-  const int e = blockIdx.x / tiles_n;
-  const int tn = blockIdx.x - e * tiles_n;
-  const int row0 = __builtin_amdgcn_readfirstlane(offsets[e]);
-  const int rows = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - row0;
-  if (rows <= 0) return;                 // no tokens routed here: nothing to read
+struct Item {
+  int row_begin;   // first row of x / y
+  int rows;        // rows of this item, 1..RB
+  int expert;
+};
 
+// Work item `item` in expert order (expert e owns ceil(r_e / RB) consecutive
+// items).  Every lane gets the same answer; false when `item` is past the
+// last one.  Lane l inspects experts e0 + 4l .. e0 + 4l + 3 per round of 256.
+__device__ inline bool find_item(const int32_t* __restrict__ offsets, int experts, int item, Item& out) {
+  const int lane = lane_id();
+  int base = 0;
+  for (int e0 = 0; e0 < experts; e0 += 256) {
+    const int eb = e0 + 4 * lane;
+    int o[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) o[j] = offsets[min(eb + j, experts)];
+    int cnt[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = eb + j < experts ? max(o[j + 1] - o[j], 0) : 0;
+      cnt[j] = (r + RB - 1) / RB;
+      sum += cnt[j];
+    }
+    int incl = sum;   // inclusive prefix sum over lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (item < base + total) {
+      const uint64_t hit = __ballot(base + incl > item);
+      const int L = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+      int before = base + __builtin_amdgcn_readlane(incl - sum, L);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = __builtin_amdgcn_readlane(cnt[j], L);
+        if (item < before + c) {
+          const int rb = item - before;
+          const int first = __builtin_amdgcn_readlane(o[j], L) + rb * RB;
+          const int last = __builtin_amdgcn_readlane(o[j + 1], L);
+          out.row_begin = first;
+          out.rows = min(RB, last - first);
+          out.expert = e0 + 4 * L + j;
+          return true;
+        }
+        before += c;
+      }
+      return false;   // unreachable with consistent counts
+    }
+    base += total;
+  }
+  return false;
+}
+
+// f16x2 {s, s} for half `idx` (0..3) of the dword pair (lo, hi).
+__device__ inline f16x2 pick_scale(uint32_t lo, uint32_t hi, uint32_t sel) {
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, sel));
+}
+
+// One item of MB 16-row blocks (rows <= 16 * MB).  G is the group size; ALIGNED:
+// each scale row starts on a 16-byte (G = 32) or 4-byte (G = 128) boundary, so
+// one vector load brings a K step's scales.
+//
+// Weight loads cover whole 128-byte lines: a load instruction reads 8 rows x
+// 128 bytes (8 lanes per row), which is what the memory system serves without
+// refetching (a load of 16 rows x 64 bytes, the MFMA operand shape, fetches
+// some lines twice).  Each lane's 16 bytes are written to a per-wave LDS tile
+// [16 rows][128 B] and read back in operand layout (lane = row li, 32 k of
+// slice lq).  Inside a row the 16-byte slots are XOR-swizzled by (row / 2) so
+// the operand reads hit distinct banks; the swizzle is applied to which piece
+// a lane loads, so the LDS write stays one contiguous 1 KB per instruction.
+template <int G, bool ALIGNED, int MB>
+__device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed_e,
+                                          const uint16_t* __restrict__ scales_e, uint16_t* __restrict__ y,
+                                          int N, int K, int rows_total, const Item& it, int band, uint8_t* lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lq = lane >> 4;              // K quarter of the MFMA operands
-  const int li = lane & 15;
-  const int nw = tn * BN + wave * kWaveN;
+  const int lq = lane >> 4;   // which 32 k of a chunk (and which 4 columns of an output block)
+  const int li = lane & 15;   // column within a block (and row within an output block)
+  const int nw = band * BN + wave * kWaveN;
 
-  const int KCH = (K + KC - 1) / KC;
-  const uint32_t row_w = (uint32_t)K >> 1;                      // packed bytes per weight row
-  const uint32_t spr = (uint32_t)K >> (5 + gshift);            // scales per weight row
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed + (size_t)e * N * (K >> 3), (uint32_t)N * row_w);
-  const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales + (size_t)e * N * spr, (uint32_t)N * spr * 2u);
+  const uint32_t row_w = (uint32_t)K >> 1;                 // packed bytes per weight row
+  const uint32_t spr = (uint32_t)(K / G);                  // scales per weight row
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed_e, (uint32_t)N * row_w);
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales_e, (uint32_t)N * spr * 2u);
   const uint32_t kbytes = (uint32_t)K * 2u;
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)rows_total * kbytes);
+  const int steps = (K + KS - 1) / KS;
 
-  auto load_w = [&](int c, u32x4 (&w)[kNB], uint32_t (&s)[kNB]) {
-    const int k = c * KC + lq * 32;
+  // ---- whole-line weight loads: instruction i of block b reads rows 8 i .. 8 i + 7 ----
+  uint32_t woff[kNB][2];   // per-lane byte offset of the first step (out of range: invalid row)
+  int klim[2];             // step s is inside K for this lane while KS * s < klim
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * i + (lane >> 3);                     // row of the block tile
+    const int q = (lane & 7) ^ ((r >> 1) & 7);             // 16-byte piece of the 128-byte line
+    klim[i] = K - 32 * q;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      const int n = nw + b * 16 + li;
-      const bool ok = c < KCH && n < N && k < K;
-      const uint32_t woff = ok ? (uint32_t)n * row_w + (uint32_t)k / 2u : kOutOfRange;
-      const uint32_t soff = ok ? ((uint32_t)n * spr + ((uint32_t)k >> (5 + gshift))) * 2u : kOutOfRange;
-      w[b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff, 0, kStream));
-      s[b] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff, 0, 0);
+      const int n = nw + b * 16 + r;
+      woff[b][i] = n < N ? (uint32_t)n * row_w + 16u * (uint32_t)q : kOutOfRange;
+    }
+  }
+  auto load_raw = [&](int s, int b, int i) -> u32x4 {
+    const uint32_t off = KS * s < klim[i] ? woff[b][i] : kOutOfRange;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 128 * s, kStream));
+  };
+  // per-wave transpose tile: [block][16 rows][128 B]
+  uint8_t* tile = lds + kTileBase + wave * kTileWave;
+  uint8_t* tile_w = tile + 16 * lane;
+  const uint32_t swz = (uint32_t)((li >> 1) & 7);
+  const uint8_t* tile_r0 = tile + li * 128 + 16 * ((uint32_t)lq ^ swz);         // chunk 0 of the step
+  const uint8_t* tile_r1 = tile + li * 128 + 16 * ((uint32_t)(4 + lq) ^ swz);   // chunk 1
+
+  // ---- scales, in operand layout (column nw + 16 b + li) ----
+  uint32_t sbase[kNB];
+  bool colok[kNB];
+#pragma unroll
+  for (int b = 0; b < kNB; ++b) {
+    const int n = nw + b * 16 + li;
+    colok[b] = n < N;
+    sbase[b] = (uint32_t)n * spr * 2u;
+  }
+  // G = 32, aligned: groups 8 s .. 8 s + 7 of the step
+  auto load_s32 = [&](int s, int b) -> u32x4 {
+    const uint32_t off = (colok[b] && 8 * s < (int)spr) ? sbase[b] + 16u * (uint32_t)s : kOutOfRange;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0));
+  };
+  // G = 128, aligned: groups 2 s, 2 s + 1
+  auto load_s128 = [&](int s, int b) -> uint32_t {
+    const uint32_t off = (colok[b] && 2 * s < (int)spr) ? sbase[b] + 4u * (uint32_t)s : kOutOfRange;
+    return __builtin_amdgcn_raw_buffer_load_b32(sres, off, 0, 0);
+  };
+  // any alignment: the group of k = 128 c + 32 lq, chunk c = 2 s + h
+  auto load_s16 = [&](int s, int h, int b) -> uint32_t {
+    const int k = KC * (2 * s + h) + 32 * lq;
+    const uint32_t off = (colok[b] && k < K) ? sbase[b] + 2u * (uint32_t)(k / G) : kOutOfRange;
+    return __builtin_amdgcn_raw_buffer_load_b16(sres, off, 0, 0);
+  };
+
+  // ---- activation staging: thread -> row tid / 16, pieces (tid % 16) + 16 p of a step ----
+  const int xr = tid >> 4;
+  const int xp = tid & 15;
+  const bool xrow_ok = xr < it.rows;
+  const uint32_t xrow_off = (uint32_t)(it.row_begin + xr) * kbytes;
+  auto load_x = [&](int s, u32x4 (&v)[kXPieces]) {
+#pragma unroll
+    for (int p = 0; p < kXPieces; ++p) {
+      const int k = KS * s + 8 * (xp + 16 * p);
+      const uint32_t off = (xrow_ok && k < K) ? xrow_off + 2u * (uint32_t)k : kOutOfRange;
+      v[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
     }
   };
-  // one 16-byte group of 8 activations per thread: 32 rows x 16 groups
-  const int a_row = tid >> 4, a_grp = tid & 15;
-  auto load_x = [&](int pass_row0, int c) -> u32x4 {
-    const int r = pass_row0 + a_row;
-    const int k = c * KC + a_grp * 8;
-    const uint32_t off = (r < rows && k < K) ? (uint32_t)(row0 + r) * kbytes + (uint32_t)k * 2u : kOutOfRange;
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+  auto store_x = [&](int s, const u32x4 (&v)[kXPieces]) {
+    uint8_t* dst = lds + (s & 1) * kABuf + xr * kAPitch + xp * 16;
+#pragma unroll
+    for (int p = 0; p < kXPieces; ++p) *reinterpret_cast<u32x4*>(dst + 256 * p) = permute_a(v[p]);
   };
 
-  for (int p0 = 0; p0 < rows; p0 += BMP) {
-    f32x4 acc[kMB][kNB];
+  // ---- prologue: kDepth steps of weights and scales, first activation block ----
+  u32x4 raw[kDepth][kNB][2];
+  u32x4 s32[kDepth][kNB];
+  uint32_t s128[kDepth][kNB];
+  uint32_t s16[kDepth][kNB][2];
+  auto issue_step = [&](int s, int slot) {
 #pragma unroll
-    for (int i = 0; i < kMB; ++i)
+    for (int b = 0; b < kNB; ++b) {
+      raw[slot][b][0] = load_raw(s, b, 0);
+      raw[slot][b][1] = load_raw(s, b, 1);
+      if constexpr (ALIGNED && G == 32) s32[slot][b] = load_s32(s, b);
+      if constexpr (ALIGNED && G == 128) s128[slot][b] = load_s128(s, b);
+      if constexpr (!ALIGNED) { s16[slot][b][0] = load_s16(s, 0, b); s16[slot][b][1] = load_s16(s, 1, b); }
+    }
+  };
 #pragma unroll
-      for (int b = 0; b < kNB; ++b) acc[i][b] = f32x4{};
+  for (int d = 0; d < kDepth; ++d) issue_step(d, d);
+  u32x4 xv[kXPieces];
+  load_x(0, xv);
+  store_x(0, xv);
+  if (steps > 1) load_x(1, xv);
+  __syncthreads();
 
-    u32x4 wq[kDepth][kNB];
-    uint32_t ws[kDepth][kNB];
+  f32x4 acc[MB][kNB];
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) load_w(d, wq[d], ws[d]);
-    u32x4 xa = load_x(p0, 0);
-    *reinterpret_cast<u32x4*>(As + a_row * kAPitch + a_grp * 16) = permute_a(xa);
-    __syncthreads();
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) acc[i][b] = f32x4{};
 
-    for (int cb = 0; cb < KCH; cb += kDepth) {
+  // per-lane selector of half lq of a dword pair, broadcast to both halves
+  const uint32_t sel_lq = (uint32_t)(2 * lq) * 0x00010001u + (uint32_t)(2 * lq + 1) * 0x01000100u;
+  // B-operand rows: this lane reads row li (+16 i), k 32 lq + 8 w of chunk h
+  const uint8_t* xfrag = lds + li * kAPitch + 64 * lq;
+
+  auto step = [&](int s, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    // transpose this step's weight lines into operand layout
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int c = cb + d;
-        if (c < KCH) {
-          const bool more = c + 1 < KCH;
-          if (more) xa = load_x(p0, c + 1);
-          const uint8_t* at = As + (c & 1) * kATile;
+    for (int b = 0; b < kNB; ++b) {
+      *reinterpret_cast<u32x4*>(tile_w + b * 2048) = raw[slot][b][0];
+      *reinterpret_cast<u32x4*>(tile_w + b * 2048 + 1024) = raw[slot][b][1];
+    }
+    u32x4 wq[2][kNB];
+    f16x2 sv[2][kNB];
 #pragma unroll
-          for (int s = 0; s < KC / 32; ++s) {
-            f16x8 bop[kNB];
+    for (int b = 0; b < kNB; ++b) {
+      wq[0][b] = *reinterpret_cast<const u32x4*>(tile_r0 + b * 2048);
+      wq[1][b] = *reinterpret_cast<const u32x4*>(tile_r1 + b * 2048);
 #pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-              const uint32_t q = s == 0 ? wq[d][b].x : (s == 1 ? wq[d][b].y : (s == 2 ? wq[d][b].z : wq[d][b].w));
-              const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)ws[d][b]);
-              bop[b] = dequant_word(q, f16x2{sv, sv});
-            }
-#pragma unroll
-            for (int i = 0; i < kMB; ++i) {
-              const u32x4 av = *reinterpret_cast<const u32x4*>(at + (i * 16 + li) * kAPitch + (4 * lq + s) * 16);
-              const f16x8 aop = __builtin_bit_cast(f16x8, av);
-#pragma unroll
-              for (int b = 0; b < kNB; ++b)
-                acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[b], acc[i][b], 0, 0, 0);
-            }
-          }
-          load_w(c + kDepth, wq[d], ws[d]);   // refill this slot (past the end: no memory access)
-          if (more) *reinterpret_cast<u32x4*>(As + ((c + 1) & 1) * kATile + a_row * kAPitch + a_grp * 16) =
-              permute_a(xa);
-          __syncthreads();
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (!ALIGNED) {
+          const _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)s16[slot][b][h]);
+          sv[h][b] = f16x2{v, v};
+        } else if constexpr (G == 32) {
+          const u32x4 v = s32[slot][b];
+          sv[h][b] = h ? pick_scale(v.z, v.w, sel_lq) : pick_scale(v.x, v.y, sel_lq);
+        } else {
+          const uint32_t v = s128[slot][b];
+          sv[h][b] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v, v, h ? 0x03020302u : 0x01000100u));
         }
       }
     }
+    // refill the ring slot kDepth steps ahead (past the end: no memory access)
+    issue_step(s + kDepth, slot);
 
-    // lane holds column li of each block, rows 4 * lq + r
+    const uint8_t* xb = xfrag + (s & 1) * kABuf;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f16x8 xf[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          xf[i] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(xb + i * 16 * kAPitch + 256 * h + 16 * w));
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+          const u32x4 wv = wq[h][b];
+          const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
+          const f16x8 wf = dequant_word(q, sv[h][b]);
+#pragma unroll
+          for (int i = 0; i < MB; ++i) acc[i][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf[i], acc[i][b], 0, 0, 0);
+        }
+      }
+    }
+    if (s + 1 < steps) {
+      store_x(s + 1, xv);
+      if (s + 2 < steps) load_x(s + 2, xv);
+      __syncthreads();
+    }
+  };
+  static_assert(kDepth == 2, "the step loop alternates two ring slots");
+  for (int s = 0; s < steps; s += 2) {
+    step(s, std::integral_constant<int, 0>{});
+    if (s + 1 < steps) step(s + 1, std::integral_constant<int, 1>{});
+  }
+
+  // ---- epilogue: lane holds columns 4 lq .. 4 lq + 3 of block b for row li (+16 i) ----
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = i * 16 + li;
+    const int row = it.row_begin + r;
+    if (r >= it.rows || row < 0 || row >= rows_total) continue;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      const int n = nw + b * 16 + li;
-      if (n >= N) continue;
+      const int n0 = nw + b * 16 + 4 * lq;
+      uint16_t h[4];
 #pragma unroll
-      for (int i = 0; i < kMB; ++i) {
+      for (int j = 0; j < 4; ++j) h[j] = float_to_half_bits(acc[i][b][j]);
+      uint16_t* dst = y + (size_t)row * N + n0;
+      if ((N & 3) == 0 && n0 + 3 < N) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = p0 + i * 16 + 4 * lq + r;
-          if (m < rows) y[(size_t)(row0 + m) * N + n] = float_to_half_bits(acc[i][b][r]);
-        }
+        for (int j = 0; j < 4; ++j)
+          if (n0 + j < N) dst[j] = h[j];
       }
     }
   }
+}
+
+template <int G, bool ALIGNED>
+__global__ void __launch_bounds__(kThreads)
+grouped_gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
+                    const uint16_t* __restrict__ scales, const int32_t* __restrict__ offsets,
+                    uint16_t* __restrict__ y, int experts, int N, int K, int rows_total, int bands) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+
+  // Consecutive workgroup ids go to different XCDs (round robin over 8): the
+  // bands of one item take ids 8 apart, so they run on the same XCD.
+  const int bid = blockIdx.x;
+  const int item = (bid / (8 * bands)) * 8 + (bid & 7);
+  const int band = (bid >> 3) % bands;
+
+  Item it;
+  if (!find_item(offsets, experts, item, it) || it.rows <= 0) return;
+
+  const size_t e = (size_t)it.expert;
+  const uint32_t* pe = packed + e * (size_t)N * (size_t)(K >> 3);
+  const uint16_t* se = scales + e * (size_t)N * (size_t)(K / G);
+  if (it.rows > 16)
+    item_body<G, ALIGNED, 2>(x, pe, se, y, N, K, rows_total, it, band, lds);
+  else
+    item_body<G, ALIGNED, 1>(x, pe, se, y, N, K, rows_total, it, band, lds);
 }
 
 }  // namespace
@@ -157,11 +367,29 @@ grouped_gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__
 hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                                const int32_t* offsets, uint16_t* y, int experts, int rows, int n, int k,
                                int group, const DeviceInfo&, hipStream_t stream) {
-  const int tiles_n = (n + BN - 1) / BN;
-  const int gshift = group == 128 ? 2 : 0;
+  const int bands = (n + BN - 1) / BN;
+  // sum over experts of ceil(r_e / RB) <= experts + ceil(rows / RB); rounded up to whole XCD rounds
+  const int64_t items = ((int64_t)experts + (rows + RB - 1) / RB + 7) / 8 * 8;
+  const int64_t blocks = items * bands;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int spr = k / group;
   (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3(experts * tiles_n), dim3(kThreads), 0, stream, x, packed, scales,
-                     offsets, y, n, k, gshift, tiles_n, rows);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (group == 32) {
+    if (spr % 8 == 0)
+      hipLaunchKernelGGL((grouped_gemm_kernel<32, true>), grid, block, 0, stream, x, packed, scales, offsets, y,
+                         experts, n, k, rows, bands);
+    else
+      hipLaunchKernelGGL((grouped_gemm_kernel<32, false>), grid, block, 0, stream, x, packed, scales, offsets, y,
+                         experts, n, k, rows, bands);
+  } else {
+    if (spr % 2 == 0)
+      hipLaunchKernelGGL((grouped_gemm_kernel<128, true>), grid, block, 0, stream, x, packed, scales, offsets, y,
+                         experts, n, k, rows, bands);
+    else
+      hipLaunchKernelGGL((grouped_gemm_kernel<128, false>), grid, block, 0, stream, x, packed, scales, offsets, y,
+                         experts, n, k, rows, bands);
+  }
   return hipGetLastError();
 }
 
