@@ -17,11 +17,15 @@
 //   its eight waves owns 32 columns (two 16-column MFMA blocks).  The two bands
 //   of an item are placed on the same XCD, so their activation rows meet in one
 //   L2.
-// * Each lane streams 16-byte packed chunks (32 consecutive k of one column) one
-//   K step (4 chunks, 512 k) ahead of use and dequantises them in registers;
-//   the group scales arrive by one vector load per step and block.
-// * The item's activation rows are staged in LDS 512 k at a time, double
-//   buffered, with one workgroup barrier per K step; the next step's rows are
+// * Weights are read in K steps of 256 k (one 128-byte line per weight row):
+//   each load instruction covers 8 rows x 128 bytes, since loads of the MFMA
+//   operand shape (16 rows x 64 bytes) make the memory system fetch some lines
+//   twice (FETCH_SIZE 186-203 MB against 172 MB per launch).  The lines go
+//   through a per-wave LDS tile into operand layout and are dequantised in
+//   registers; one step is in flight ahead of use (deeper rings measured
+//   slower).  The group scales arrive by one vector load per step and block.
+// * The item's activation rows are staged in LDS one step at a time, double
+//   buffered, with one workgroup barrier per step; the next step's rows are
 //   loaded into registers a full step before they are written.
 // * The weights are the MFMA's A operand (v_mfma_f32_16x16x32_f16, 16 columns
 //   x 32 k) and the activations its B operand, so a lane ends with four
@@ -37,21 +41,22 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int BN = 256;                    // output columns per workgroup
 constexpr int kWaveN = 32;                 // columns per wave
+constexpr int BN = kWaves * kWaveN;        // output columns per workgroup
 constexpr int kNB = kWaveN / 16;           // 16-column MFMA blocks per wave
 constexpr int RB = 32;                     // rows per work item
 constexpr int KC = 128;                    // k per chunk: 16 bytes per lane and block in operand layout
 constexpr int KS = 2 * KC;                 // k per K step: one 128-byte line per weight row
-constexpr int kDepth = 2;                  // K steps of weights in flight
+constexpr int kDepth = 1;                  // K steps of weights in flight (a deeper ring measured slower)
 constexpr int kAPitch = KS * 2 + 16;       // bytes per staged activation row: rows shift by 4 banks
 constexpr int kABuf = RB * kAPitch;        // one staged activation block
-constexpr int kXPieces = RB * KS / 8 / kThreads;   // 16-byte activation pieces per thread and step
+constexpr int kRowThreads = kThreads / RB;        // threads staging one activation row
+constexpr int kXPieces = KS / 8 / kRowThreads;     // 16-byte activation pieces per thread and step
 constexpr int kTileWave = kNB * 16 * 128;  // per-wave weight transpose tile
 constexpr int kTileBase = 2 * kABuf;
 constexpr int kLds = kTileBase + kWaves * kTileWave;
 
-static_assert(kXPieces == 2, "activation staging assumes two pieces per thread");
+static_assert(kXPieces >= 1 && kXPieces * kRowThreads * 8 == KS, "activation staging covers a step");
 static_assert(kLds <= 80 * 1024, "two workgroups per CU");
 
 struct Item {
@@ -199,14 +204,14 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
   };
 
   // ---- activation staging: thread -> row tid / 16, pieces (tid % 16) + 16 p of a step ----
-  const int xr = tid >> 4;
-  const int xp = tid & 15;
+  const int xr = tid / kRowThreads;
+  const int xp = tid % kRowThreads;
   const bool xrow_ok = xr < it.rows;
   const uint32_t xrow_off = (uint32_t)(it.row_begin + xr) * kbytes;
   auto load_x = [&](int s, u32x4 (&v)[kXPieces]) {
 #pragma unroll
     for (int p = 0; p < kXPieces; ++p) {
-      const int k = KS * s + 8 * (xp + 16 * p);
+      const int k = KS * s + 8 * (xp + kRowThreads * p);
       const uint32_t off = (xrow_ok && k < K) ? xrow_off + 2u * (uint32_t)k : kOutOfRange;
       v[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
     }
@@ -214,7 +219,7 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
   auto store_x = [&](int s, const u32x4 (&v)[kXPieces]) {
     uint8_t* dst = lds + (s & 1) * kABuf + xr * kAPitch + xp * 16;
 #pragma unroll
-    for (int p = 0; p < kXPieces; ++p) *reinterpret_cast<u32x4*>(dst + 256 * p) = permute_a(v[p]);
+    for (int p = 0; p < kXPieces; ++p) *reinterpret_cast<u32x4*>(dst + 16 * kRowThreads * p) = permute_a(v[p]);
   };
 
   // ---- prologue: kDepth steps of weights and scales, first activation block ----
@@ -307,10 +312,12 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
       __syncthreads();
     }
   };
-  static_assert(kDepth == 2, "the step loop alternates two ring slots");
-  for (int s = 0; s < steps; s += 2) {
+  static_assert(kDepth == 1 || kDepth == 2, "the step loop cycles through the ring slots");
+  for (int s = 0; s < steps; s += kDepth) {
     step(s, std::integral_constant<int, 0>{});
-    if (s + 1 < steps) step(s + 1, std::integral_constant<int, 1>{});
+    if constexpr (kDepth == 2) {
+      if (s + 1 < steps) step(s + 1, std::integral_constant<int, kDepth - 1>{});
+    }
   }
 
   // ---- epilogue: lane holds columns 4 lq .. 4 lq + 3 of block b for row li (+16 i) ----
