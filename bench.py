@@ -81,35 +81,86 @@ def make_pool(torch, packed_np, scales_np, min_bytes=POOL_BYTES):
     return pool
 
 
-def timed(torch, fn, steps, warmup):
-    """Mean ms per call of fn(i) over `steps` calls, HIP events on the current stream."""
+def _graph_of(torch, fn, steps):
+    """fn(0) .. fn(steps - 1) captured in one HIP graph, or None if capture fails.
+
+    The launches go to the capture stream (the binding launches on torch's
+    current stream).  None of the captured kernels issues a memset."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
+    except Exception as e:  # capture unsupported here: time eager launches instead
+        print(f"bench: graph capture failed ({e}); timing eager launches", file=sys.stderr)
+        return None
+
+
+def _check_replay(torch, fn, steps, outputs):
+    """The graph's last launches must have left the same bits as an eager launch."""
+    if not outputs:
+        return
+    got = [o.clone() for o in outputs]
+    fn(steps - 1)
+    torch.cuda.synchronize()
+    for a, b in zip(got, outputs):
+        if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
+            raise RuntimeError("graph replay result differs from the eager launch")
+
+
+def timed(torch, fn, steps, warmup, graph=False, outputs=()):
+    """Mean ms per call of fn(i) over `steps` calls, HIP events on the current stream.
+
+    graph=True: the calls are captured once in a HIP graph and replayed, so the
+    host's per-call launch cost (Python + ctypes) does not enter the timing."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    g = _graph_of(torch, fn, steps) if graph else None
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        fn(i)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            fn(i)
     stop.record()
     torch.cuda.synchronize()
+    if g is not None:
+        _check_replay(torch, fn, steps, outputs)
     return start.elapsed_time(stop) / steps
 
 
-def per_launch(torch, fn, steps, batches=5):
+def per_launch(torch, fn, steps, batches=5, graph=False, outputs=()):
     """Mean ms per launch of fn(i): `batches` runs of `steps` back-to-back launches,
-    each run bracketed by one pair of events on the launch stream.  Returns
-    (mean, median over the runs)."""
+    each run bracketed by one pair of events on the launch stream (graph=True:
+    each run is one replay of a captured graph of the `steps` launches).
+    Returns (mean, median over the runs)."""
     fn(0)
     torch.cuda.synchronize()
+    g = _graph_of(torch, fn, steps) if graph else None
     per = []
     for b in range(batches):
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
-        for i in range(steps):
-            fn(b * steps + i)
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(steps):
+                fn(b * steps + i)
         stop.record()
         torch.cuda.synchronize()
         per.append(start.elapsed_time(stop) / steps)
+    if g is not None:
+        _check_replay(torch, fn, steps, outputs)
     return float(np.mean(per)), float(np.median(per))
 
 
@@ -156,7 +207,7 @@ def decode_component(torch, w4, synth, args):
         p, s = pool_d[i % len(pool_d)]
         w4.gemv(xd_t, p, s, 128, out=yd)
 
-    ms = timed(torch, step, args.steps, args.warmup)
+    ms = timed(torch, step, args.steps, args.warmup, graph=True, outputs=(yu, yd))
     step_bytes = dense_bytes(1, up.n, up.k, 128) + dense_bytes(1, down.n, down.k, 128)
 
     def one_up(i):
@@ -167,8 +218,8 @@ def decode_component(torch, w4, synth, args):
         p, s = pool_d[i % len(pool_d)]
         w4.gemv(xd_t, p, s, 128, out=yd)
 
-    up_mean, up_med = per_launch(torch, one_up, args.steps)
-    dn_mean, dn_med = per_launch(torch, one_down, args.steps)
+    up_mean, up_med = per_launch(torch, one_up, args.steps, graph=True, outputs=(yu,))
+    dn_mean, dn_med = per_launch(torch, one_down, args.steps, graph=True, outputs=(yd,))
     launch_ms = (up_mean + dn_mean) / 2
     launch_bytes = dense_bytes(1, up.n, up.k, 128)   # the two launches move equal bytes
     return {
@@ -198,7 +249,7 @@ def np4_component(torch, w4, synth, args):
             pp, ss = pool[i % len(pool)]
             w4.gemv(xt, pp, ss, c.group, out=y)
 
-        mean, med = per_launch(torch, one, args.steps)
+        mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
         b = dense_bytes(c.m, c.n, c.k, c.group)
         out[name] = {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
                      "gbs": b / (mean * 1e-3) / 1e9, "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -250,7 +301,7 @@ def moe_component(torch, w4, synth, args):
         pp, ss = pool[i % len(pool)]
         w4.grouped_gemm(xs, pp, ss, offs, c.group, out=y)
 
-    mean, med = per_launch(torch, one, args.steps)
+    mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
     b = c.experts * c.n * c.k // 2 + c.experts * c.n * (c.k // c.group) * 2 + rows * c.k * 2 + rows * c.n * 2 \
         + (c.experts + 1) * 4
     fl = dense_flops(rows, c.n, c.k)
@@ -265,7 +316,7 @@ def moe_component(torch, w4, synth, args):
         pp, ss = pool[i % len(pool)]
         w4.grouped_gemm(xs2, pp, ss, offs2, c.group, out=y)
 
-    mean2, _ = per_launch(torch, one_skewed, args.steps)
+    mean2, _ = per_launch(torch, one_skewed, args.steps, graph=True, outputs=(y,))
     used = int(np.count_nonzero(rs.counts))
     b2 = used * (c.n * c.k // 2 + c.n * (c.k // c.group) * 2) + rows * c.k * 2 + rows * c.n * 2 + (c.experts + 1) * 4
     return {"launch_ms": mean, "launch_ms_median": med, "bytes": b, "gbs": b / (mean * 1e-3) / 1e9,
@@ -558,7 +609,8 @@ def main():
         "dtype": "f16 activations x int4 weights, f32 accumulate",
         "data": "synthetic (seeded Gaussian weights quantised int4 sym g128; fp16 N(0,1) activations)",
         "config": {"workload": "decode GEMV M=1, 27B-like dense FFN: up K=5120->N=17408 + down K=17408->N=5120, g128",
-                   "m": 1, "group": 128, "rotating_weight_pool_bytes": POOL_BYTES},
+                   "m": 1, "group": 128, "rotating_weight_pool_bytes": POOL_BYTES,
+                   "launch": "timed launches replayed from one HIP graph (GEMM: host launches)"},
         "roofline": {"bound": "hbm", "achieved": round(k["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": k["name"], "launch_us": round(k["launch_ms"] * 1e3, 3),

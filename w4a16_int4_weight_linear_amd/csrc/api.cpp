@@ -111,6 +111,12 @@ int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
+  // Three or four activation rows: the MFMA kernel (faster there; at two rows the
+  // per-lane kernel is), while its activations fit in LDS.
+  int mb = 0;
+  size_t mlds = 0;
+  if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, dev, &mb, &mlds))
+    return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)n, (int)k, group, mb, mlds, dev, st));
   const w4a16::GemvPlan plan = w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev);
   if (!plan.ok) return W4A16_ERR_SHAPE;
   return status_of(w4a16::launch_gemv(x, packed, scales, y, (int)m, (int)n, (int)k, group, plan, dev, st));

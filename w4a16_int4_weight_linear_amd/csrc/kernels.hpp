@@ -33,6 +33,13 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t
                        int m, int n, int k, int group, const GemvPlan& plan, const DeviceInfo& dev,
                        hipStream_t stream);
 
+// ---- batched decode GEMV on MFMA, 2 <= m <= 4 (gemv_mfma.hip) ----
+// Workgroup count and LDS bytes; false if the activations do not fit in LDS.
+bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, size_t* lds);
+hipError_t launch_gemv_mfma(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
+                            int n, int k, int group, int blocks, size_t lds, const DeviceInfo& dev,
+                            hipStream_t stream);
+
 // ---- prefill GEMM (gemm.hip) ----
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int group, const DeviceInfo& dev);
 hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
