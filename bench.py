@@ -407,9 +407,10 @@ def trace_summary(trace_csv, command):
     from collections import defaultdict
     labels = {"gemm_kernel": ["M=512", "M=4096"],
               "gemv_kernel<1>": ["one of up 5120->17408 / down 17408->5120 (same bytes)"],
-              "gemv_kernel<4>": ["N=5120", "N=17408"],
-              "grouped_gemm_kernel": ["256 experts, 4096 routed rows, N=512, K=2048, g32"]}
-    files = {"gemv_kernel<1>": "gemv_m1_decode_27b_ffn", "gemv_kernel<4>": "gemv_m4_np4_27b_ffn",
+              "gemv_mfma_kernel<4": ["N=5120", "N=17408"],
+              "grouped_gemm_kernel": ["256 experts x [512 x 2048] g32, 4096 routed rows, uniform top-8",
+                                      "same bank, Zipf-skewed top-8 (244 experts used)"]}
+    files = {"gemv_kernel<1>": "gemv_m1_decode_27b_ffn", "gemv_mfma_kernel<4": "gemv_m4_np4_27b_ffn",
              "gemm_kernel": "gemm_prefill_27b_ffn", "grouped_gemm_kernel": "grouped_gemm_moe_256e"}
     groups = defaultdict(list)
     with open(trace_csv) as f:
@@ -431,14 +432,23 @@ def trace_summary(trace_csv, command):
         return [d[cuts[i]:cuts[i + 1]] for i in range(len(cuts) - 1)]
 
     out = defaultdict(list)
-    for (k, grid, wg, lds, vgpr, agpr), d in sorted(groups.items()):
-        base = "gemm_kernel" if k.startswith("gemm_kernel") else k
-        if base not in files:
-            continue
+    per_base = defaultdict(list)
+    for key in sorted(groups, key=lambda t: (t[0], t[1])):
+        base = next((b for b in files if key[0].startswith(b)), None)
+        if base is not None:
+            per_base[base].append(key)
+    for base, keys in per_base.items():
         lab = labels[base]
-        for name, c in zip(lab, clusters(d, len(lab))):
-            out[base].append((k, name, grid, wg, lds, vgpr, agpr, len(c), statistics.mean(c),
-                              statistics.median(c), min(c), max(c)))
+        # Workloads on distinct grids (one per label, in order of grid size) need no
+        # clustering; workloads sharing a grid are split at the duration gaps.
+        by_grid = len(keys) == len(lab) and len(lab) > 1
+        for j, key in enumerate(keys):
+            k, grid, wg, lds, vgpr, agpr = key
+            d = groups[key]
+            named = [(lab[j], sorted(d))] if by_grid else list(zip(lab, clusters(d, len(lab))))
+            for name, c in named:
+                out[base].append((k, name, grid, wg, lds, vgpr, agpr, len(c), statistics.mean(c),
+                                  statistics.median(c), min(c), max(c)))
     for base, lst in out.items():
         path = os.path.join(ROOT, "profiles", f"{files[base]}.kernel_trace.md")
         with open(path, "w") as f:
