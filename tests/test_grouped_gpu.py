@@ -37,6 +37,7 @@ def offsets_from_counts(counts):
 # passes), ragged n, a K tail (k % 128 != 0), both group sizes.
 EXACT_CASES = [
     (4, 256, 128, 32, [3, 0, 17, 1]),
+    (3, 260, 384, 128, [33, 2, 65]),        # odd scales per row (3): per-chunk scale loads
     (3, 300, 256, 128, [40, 0, 5]),
     (5, 64, 2080, 32, [0, 0, 70, 2, 33]),
     (2, 512, 2048, 32, [1, 29]),
@@ -116,3 +117,22 @@ def test_grouped_equals_dense_per_expert_and_permutation(w4):
     assert np.array_equal(y2.view(np.uint16), y[order].view(np.uint16))
     y3 = run_grouped(w4, xs, packed, scales, r.offsets, 32)
     assert np.array_equal(y3.view(np.uint16), y.view(np.uint16))
+
+
+def test_grouped_many_experts_work_item_scan(w4):
+    """More than 256 experts (the device-side work-item scan takes several rounds of
+    256), with empty experts, single rows, and experts of 32, 33 and 97 rows (one,
+    two and four 32-row work items) spread over all rounds."""
+    rng = np.random.default_rng(7300)
+    experts, n, k = 700, 64, 256
+    counts = np.zeros(experts, np.int64)
+    picks = rng.choice(experts, 120, replace=False)
+    counts[picks] = rng.integers(1, 6, size=120)
+    counts[[0, 255, 256, 511, 512, 699]] = [32, 33, 97, 1, 64, 40]
+    q, s = exact_bank(rng, experts, n, k, 32)
+    offs = offsets_from_counts(counts)
+    xs = synth.integer_activations(rng, int(offs[-1]), k)
+    packed = np.stack([w4.pack(q[e]) for e in range(experts)])
+    y = run_grouped(w4, xs, packed, s, offs, 32)
+    y_ref = oracle.grouped_linear(xs, np.stack([oracle.pack(q[e]) for e in range(experts)]), s, offs, 32)
+    assert_bit_exact(y, y_ref, f"E={experts} rows={int(offs[-1])}")
