@@ -70,14 +70,28 @@ def test_gemm_workload_full_size_sampled(w4, name):
 
 
 def test_gemm_matches_gemv_for_small_m(w4):
-    """Two independent kernels on the same problem agree within the oracle's bars."""
+    """Two independent kernels on the same problem agree within the oracle's bars:
+    six rows run on the GEMM kernel, rows 0-3 and 4-5 on the GEMV kernels."""
     rng = np.random.default_rng(6100)
     w = synth.weights(rng, 2000, 3072)
-    x = synth.activations(rng, 4, 3072)
+    x = synth.activations(rng, 6, 3072)
+    p, s = w4.quantize(w, 128)
+    yg = run_gemm(w4, x, p, s, 128)
+    yv = np.concatenate([host(w4.gemv(dev(x[:4]), dev(p), dev(s), 128)),
+                         host(w4.gemv(dev(x[4:]), dev(p), dev(s), 128))])
+    assert_close(yg, yv.astype(np.float64), "gemm vs gemv")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_gemm_small_m_runs_gemv_kernels(w4, m):
+    """w4a16_gemm with m <= 4 gives the GEMV kernels' bits (it dispatches to them)."""
+    rng = np.random.default_rng(6150 + m)
+    w = synth.weights(rng, 1000, 2048)
+    x = synth.activations(rng, m, 2048)
     p, s = w4.quantize(w, 128)
     yg = run_gemm(w4, x, p, s, 128)
     yv = host(w4.gemv(dev(x), dev(p), dev(s), 128))
-    assert_close(yg, yv.astype(np.float64), "gemm vs gemv")
+    assert np.array_equal(yg.view(np.uint16), yv.view(np.uint16))
 
 
 def test_gemm_deterministic(w4):

@@ -74,6 +74,21 @@ int common_dense_checks(const uint16_t* x, const uint32_t* packed, const uint16_
 
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+// The decode GEMV kernels for 1 <= m <= 4 (k > 0, arguments already checked).
+// Returns -1 when no GEMV plan fits this k (the activations do not fit in LDS).
+int gemv_dispatch(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+                  int64_t n, int64_t k, int32_t group, const DeviceInfo& dev, hipStream_t st) {
+  // Three or four activation rows: the MFMA kernel (faster there; at two rows the
+  // per-lane kernel is), while its activations fit in LDS.
+  int mb = 0;
+  size_t mlds = 0;
+  if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, dev, &mb, &mlds))
+    return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)n, (int)k, group, mb, mlds, dev, st));
+  const w4a16::GemvPlan plan = w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev);
+  if (!plan.ok) return -1;
+  return status_of(w4a16::launch_gemv(x, packed, scales, y, (int)m, (int)n, (int)k, group, plan, dev, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,15 +126,8 @@ int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
-  // Three or four activation rows: the MFMA kernel (faster there; at two rows the
-  // per-lane kernel is), while its activations fit in LDS.
-  int mb = 0;
-  size_t mlds = 0;
-  if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, dev, &mb, &mlds))
-    return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)n, (int)k, group, mb, mlds, dev, st));
-  const w4a16::GemvPlan plan = w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev);
-  if (!plan.ok) return W4A16_ERR_SHAPE;
-  return status_of(w4a16::launch_gemv(x, packed, scales, y, (int)m, (int)n, (int)k, group, plan, dev, st));
+  const int r = gemv_dispatch(x, packed, scales, y, m, n, k, group, dev, st);
+  return r < 0 ? W4A16_ERR_SHAPE : r;
 }
 
 size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group) {
@@ -142,6 +150,12 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
   const size_t need = w4a16::gemm_workspace_bytes(m, n, k, group, dev);
   if (need && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
+  // Up to four rows the product is a weight stream: the decode GEMV kernels do it
+  // in a fraction of the 128-row GEMM tile's time (the workspace is left untouched).
+  if (m <= 4) {
+    const int r = gemv_dispatch(x, packed, scales, y, m, n, k, group, dev, st);
+    if (r >= 0) return r;
+  }
   return status_of(w4a16::launch_gemm(x, packed, scales, y, (int)m, (int)n, (int)k, group,
                                       need ? workspace : nullptr, dev, st));
 }
