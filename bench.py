@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--components", default="decode,np4,prefill,moe",
+    ap.add_argument("--components", default="decode,np4,batch16,prefill,moe",
                     help="comma list of parts to measure (decode is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -254,6 +254,27 @@ def np4_component(torch, w4, synth, args):
         out[name] = {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
                      "gbs": b / (mean * 1e-3) / 1e9, "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}
     return out
+
+
+def batched_decode_component(torch, w4, synth, args):
+    """Not a graded workload: a decode step batching 16 sequences (w4a16_gemm at
+    M = 16, the weight-streaming kernel) on the 27B up-projection shape."""
+    c = synth.DENSE_CASES["gemv_np4_4x5120x17408_g128"]
+    w, _ = synth.dense_inputs(c)
+    p, s = w4.quantize(w, c.group)
+    pool = make_pool(torch, p, s)
+    x = synth.activations(np.random.default_rng(c.seed + 100), 16, c.k)
+    xt = torch.from_numpy(x).to("cuda")
+    y = torch.empty((16, c.n), dtype=torch.float16, device="cuda")
+
+    def one(i):
+        pp, ss = pool[i % len(pool)]
+        w4.gemm(xt, pp, ss, c.group, out=y)
+
+    mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+    b = dense_bytes(16, c.n, c.k, c.group)
+    return {"gemm_16x5120x17408_g128": {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
+                                         "gbs": b / (mean * 1e-3) / 1e9, "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
 def prefill_component(torch, w4, synth, args):
@@ -590,7 +611,8 @@ def main():
     res = {}
     if "decode" not in comps:
         # component runs without the headline (profiling passes): no JSON line contract
-        for name, fn in (("np4", np4_component), ("prefill", prefill_component), ("moe", moe_component)):
+        for name, fn in (("np4", np4_component), ("batch16", batched_decode_component),
+                         ("prefill", prefill_component), ("moe", moe_component)):
             if name in comps:
                 res[name] = fn(torch, w4, synth, args)
         print(json.dumps({"components": res}, default=float))
@@ -598,6 +620,8 @@ def main():
     decode = decode_component(torch, w4, synth, args)
     if "np4" in comps:
         res["np4"] = np4_component(torch, w4, synth, args)
+    if "batch16" in comps:
+        res["batch16"] = batched_decode_component(torch, w4, synth, args)
     if "prefill" in comps:
         res["prefill"] = prefill_component(torch, w4, synth, args)
     if "moe" in comps:

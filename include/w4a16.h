@@ -125,8 +125,9 @@ size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  * the state it needs for the next call, so a buffer may be reused by calls
  * that run one after another on the same stream, but not by concurrent ones.
  * A fresh workspace must be zero-filled once before its first use.  For
- * m <= 4 the product runs on the decode GEMV kernels (same result bars) and
- * the workspace is not touched; it is still validated as above.
+ * m <= 32 the product is a weight stream and runs on weight-streaming kernels
+ * (m <= 4: the decode GEMV kernels), with the same result bars; the workspace
+ * is then not touched, but it is still validated as above.
  */
 int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,

@@ -103,3 +103,34 @@ def test_gemm_deterministic(w4):
     y1 = host(w4.gemm(xd, pd, sd, 32))
     y2 = host(w4.gemm(xd, pd, sd, 32))
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+# (m, n, k, group) for 5 <= m <= 32, the weight-streaming kernel (16 rows per pass): a K tail inside
+# a line (96, 2080), a partial last activation chunk (2080, 5120, 6144), odd scale
+# counts per row (2080 g32, 384 g128), tiny N (17: two workgroups), six 16-row
+# blocks per workgroup (23040 rows over 256 workgroups), both group sizes.
+SKINNY_SHAPES = [(5, 100, 96, 32), (8, 300, 2080, 32), (13, 1000, 5120, 128), (16, 257, 384, 128),
+                 (16, 2049, 4096, 32), (11, 17, 6144, 128), (6, 23040, 512, 128),
+                 (18, 700, 1024, 32), (32, 513, 2304, 128)]   # two 16-row passes (16 + 2, 16 + 16)
+
+
+@pytest.mark.parametrize("m,n,k,group", SKINNY_SHAPES)
+def test_gemm_skinny_exact_integer_family(w4, m, n, k, group):
+    rng = np.random.default_rng(5500 + m + n + k + group)
+    x = synth.integer_activations(rng, m, k)
+    q = synth.integer_codes(rng, n, k)
+    s = synth.power_of_two_scales(rng, n, k // group, lo=-6, hi=-3)
+    y = run_gemm(w4, x, w4.pack(q), s, group)
+    assert_bit_exact(y, oracle.linear(x, oracle.pack(q), s, group), f"m={m} n={n} k={k} g={group}")
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 17408, 5120), (8, 5120, 17408)])
+def test_gemm_skinny_gaussian_27b_shapes(w4, m, n, k):
+    """Batched decode of 8 / 16 sequences on the 27B FFN's up / down shapes, every output checked."""
+    rng = np.random.default_rng(5600 + m)
+    w = synth.weights(rng, n, k)
+    x = synth.activations(rng, m, k)
+    (p, s), (p_ref, s_ref) = gaussian_sides(w4, w, 128)
+    y = run_gemm(w4, x, p, s, 128)
+    rep = assert_close(y, oracle.linear(x, p_ref, s_ref, 128), f"m={m} n={n} k={k}")
+    print(f"m={m} n={n} k={k}: {rep.message}")

@@ -156,6 +156,18 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
     const int r = gemv_dispatch(x, packed, scales, y, m, n, k, group, dev, st);
     if (r >= 0) return r;
   }
+  // Five to 32 rows (a batched decode step) are still a weight stream: one pass
+  // of the weight-streaming kernel per 16 rows (two passes beat the 128-row
+  // GEMM tiles up to 32 rows).
+  if (m <= 32 && w4a16::gemm_skinny_fits((int)(m < 16 ? m : 16), (int)n, (int)k, dev)) {
+    for (int64_t m0 = 0; m0 < m; m0 += 16) {
+      const int mm = (int)(m - m0 < 16 ? m - m0 : 16);
+      const hipError_t e = w4a16::launch_gemm_skinny(x + m0 * k, packed, scales, y + m0 * n, mm, (int)n, (int)k,
+                                                     group, dev, st);
+      if (e != hipSuccess) return W4A16_ERR_HIP;
+    }
+    return W4A16_OK;
+  }
   return status_of(w4a16::launch_gemm(x, packed, scales, y, (int)m, (int)n, (int)k, group,
                                       need ? workspace : nullptr, dev, st));
 }

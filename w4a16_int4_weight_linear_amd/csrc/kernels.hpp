@@ -40,6 +40,11 @@ hipError_t launch_gemv_mfma(const uint16_t* x, const uint32_t* packed, const uin
                             int n, int k, int group, int blocks, size_t lds, const DeviceInfo& dev,
                             hipStream_t stream);
 
+// ---- 5 <= m <= 16 rows, weight-streaming on MFMA (gemm_skinny.hip) ----
+bool gemm_skinny_fits(int m, int n, int k, const DeviceInfo& dev);
+hipError_t launch_gemm_skinny(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
+                              int n, int k, int group, const DeviceInfo& dev, hipStream_t stream);
+
 // ---- prefill GEMM (gemm.hip) ----
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int group, const DeviceInfo& dev);
 hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
