@@ -112,8 +112,9 @@ int64_t w4a16_gemv_max_k(int64_t m, int32_t group);
 
 /*
  * Bytes of device workspace w4a16_gemm needs for this problem on the current
- * device (0 means none; the pointer may then be NULL).  Returns 0 for invalid
- * shapes as well; w4a16_gemm reports those.
+ * device (0 means none; the pointer may then be NULL).  It is 0 for the
+ * weight-streaming sizes (m <= 32 where those kernels run).  Returns 0 for
+ * invalid shapes as well; w4a16_gemm reports those.
  */
 size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group);
 
@@ -126,8 +127,8 @@ size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  * that run one after another on the same stream, but not by concurrent ones.
  * A fresh workspace must be zero-filled once before its first use.  For
  * m <= 32 the product is a weight stream and runs on weight-streaming kernels
- * (m <= 4: the decode GEMV kernels), with the same result bars; the workspace
- * is then not touched, but it is still validated as above.
+ * (m <= 4: the decode GEMV kernels), with the same result bars; those need no
+ * workspace (the query returns 0) and never touch one that is passed.
  */
 int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,

@@ -74,6 +74,24 @@ int common_dense_checks(const uint16_t* x, const uint32_t* packed, const uint16_
 
 int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+// Which kernels w4a16_gemm runs: up to 32 rows the product is a weight stream
+// (m <= 4: the decode GEMV kernels while their plan fits; 5..32: the
+// weight-streaming MFMA kernel, one pass per 16 rows); otherwise the tiled GEMM,
+// the only one that uses the workspace.
+enum class GemmPath { kGemv, kSkinny, kTiled };
+
+GemmPath gemm_path(int64_t m, int64_t n, int64_t k, int32_t group, const DeviceInfo& dev) {
+  if (m <= 4) {
+    int mb = 0;
+    size_t mlds = 0;
+    if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, dev, &mb, &mlds)) return GemmPath::kGemv;
+    if (w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev).ok) return GemmPath::kGemv;
+    return GemmPath::kTiled;
+  }
+  if (m <= 32 && w4a16::gemm_skinny_fits((int)(m < 16 ? m : 16), (int)n, (int)k, dev)) return GemmPath::kSkinny;
+  return GemmPath::kTiled;
+}
+
 // The decode GEMV kernels for 1 <= m <= 4 (k > 0, arguments already checked).
 // Returns -1 when no GEMV plan fits this k (the activations do not fit in LDS).
 int gemv_dispatch(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
@@ -135,6 +153,7 @@ size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
   if (m > kMaxDim || n > kMaxDim || k > kMaxDim) return 0;
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return 0;
+  if (gemm_path(m, n, k, group, dev) != GemmPath::kTiled) return 0;
   return w4a16::gemm_workspace_bytes(m, n, k, group, dev);
 }
 
@@ -148,18 +167,13 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
-  const size_t need = w4a16::gemm_workspace_bytes(m, n, k, group, dev);
-  if (need && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
-  // Up to four rows the product is a weight stream: the decode GEMV kernels do it
-  // in a fraction of the 128-row GEMM tile's time (the workspace is left untouched).
-  if (m <= 4) {
+  const GemmPath path = gemm_path(m, n, k, group, dev);
+  if (path == GemmPath::kGemv) {
     const int r = gemv_dispatch(x, packed, scales, y, m, n, k, group, dev, st);
-    if (r >= 0) return r;
+    return r < 0 ? W4A16_ERR_SHAPE : r;   // not reached: gemm_path checked the plan
   }
-  // Five to 32 rows (a batched decode step) are still a weight stream: one pass
-  // of the weight-streaming kernel per 16 rows (two passes beat the 128-row
-  // GEMM tiles up to 32 rows).
-  if (m <= 32 && w4a16::gemm_skinny_fits((int)(m < 16 ? m : 16), (int)n, (int)k, dev)) {
+  if (path == GemmPath::kSkinny) {
+    // one pass per 16 rows (two passes beat the 128-row GEMM tiles up to 32 rows)
     for (int64_t m0 = 0; m0 < m; m0 += 16) {
       const int mm = (int)(m - m0 < 16 ? m - m0 : 16);
       const hipError_t e = w4a16::launch_gemm_skinny(x + m0 * k, packed, scales, y + m0 * n, mm, (int)n, (int)k,
@@ -168,6 +182,8 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
     }
     return W4A16_OK;
   }
+  const size_t need = w4a16::gemm_workspace_bytes(m, n, k, group, dev);
+  if (need && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
   return status_of(w4a16::launch_gemm(x, packed, scales, y, (int)m, (int)n, (int)k, group,
                                       need ? workspace : nullptr, dev, st));
 }
