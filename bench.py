@@ -444,15 +444,17 @@ def trace_summary(trace_csv, command):
             short = name.replace("w4a16::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
             key = (short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]),
                    int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]))
-            groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+            groups[key].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0))
 
     def clusters(d, n):
+        # The benchmark runs its workloads one after another: split the launches,
+        # in time order, at the n - 1 largest pauses between consecutive starts.
         d = sorted(d)
         if n <= 1 or len(d) < 2:
-            return [d]
-        gaps = sorted(range(1, len(d)), key=lambda i: d[i] - d[i - 1], reverse=True)[: n - 1]
+            return [sorted(t for _, t in d)]
+        gaps = sorted(range(1, len(d)), key=lambda i: d[i][0] - d[i - 1][0], reverse=True)[: n - 1]
         cuts = [0] + sorted(gaps) + [len(d)]
-        return [d[cuts[i]:cuts[i + 1]] for i in range(len(cuts) - 1)]
+        return [sorted(t for _, t in d[cuts[i]:cuts[i + 1]]) for i in range(len(cuts) - 1)]
 
     out = defaultdict(list)
     per_base = defaultdict(list)
@@ -468,7 +470,7 @@ def trace_summary(trace_csv, command):
         for j, key in enumerate(keys):
             k, grid, wg, lds, vgpr, agpr = key
             d = groups[key]
-            named = [(lab[j], sorted(d))] if by_grid else list(zip(lab, clusters(d, len(lab))))
+            named = [(lab[j], sorted(t for _, t in d))] if by_grid else list(zip(lab, clusters(d, len(lab))))
             for name, c in named:
                 out[base].append((k, name, grid, wg, lds, vgpr, agpr, len(c), statistics.mean(c),
                                   statistics.median(c), min(c), max(c)))
@@ -478,8 +480,8 @@ def trace_summary(trace_csv, command):
             f.write(f"# {base}: rocprofv3 kernel trace of bench.py\n\n")
             f.write("Command (from the repository root on the GPU box), then the summary:\n\n```\n"
                     f"{command}\npython3 bench.py --trace-summary <trace dir>/bench_kernel_trace.csv '<command>'\n```\n\n")
-            f.write("Launches of one kernel with the same grid are split into workloads at the largest gaps "
-                    "between their durations.\n\n")
+            f.write("Launches of one kernel with the same grid are split into workloads (run one after "
+                    "another) at the largest pauses between consecutive launch starts.\n\n")
             f.write("| kernel | workload | grid (threads) | workgroup | LDS bytes | VGPR | AGPR | launches | "
                     "mean us | median us | min us | max us |\n|---|---|---|---|---|---|---|---|---|---|---|---|\n")
             for k, name, grid, wg, lds, vgpr, agpr, n, mean, med, mn, mx in lst:
