@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--components", default="decode,np4,batch16,prefill,moe",
+    ap.add_argument("--components", default="decode,np4,batch16,swiglu,prefill,moe",
                     help="comma list of parts to measure (decode is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -275,6 +275,35 @@ def batched_decode_component(torch, w4, synth, args):
     b = dense_bytes(16, c.n, c.k, c.group)
     return {"gemm_16x5120x17408_g128": {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
                                          "gbs": b / (mean * 1e-3) / 1e9, "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+
+def swiglu_component(torch, w4, synth, args):
+    """Not a graded workload: the 27B FFN's fused gate/up projection with the SwiGLU
+    epilogue (w4a16_gemv_swiglu: 2 x 17408 interleaved rows, K = 5120, g128) at M = 1 and 4."""
+    c = synth.DENSE_CASES["gemv_up_1x5120x17408_g128"]
+    rng = np.random.default_rng(c.seed + 200)
+    wg = synth.weights(rng, c.n, c.k)
+    pg, sg = w4.quantize(wg, c.group)
+    del wg
+    wu = synth.weights(rng, c.n, c.k)
+    pu, su = w4.quantize(wu, c.group)
+    del wu
+    pool = make_pool(torch, w4.interleave_rows(pg, pu), w4.interleave_rows(sg, su))
+    out = {}
+    for m in (1, 4):
+        xt = torch.from_numpy(synth.activations(rng, m, c.k)).to("cuda")
+        y = torch.empty((m, c.n), dtype=torch.float16, device="cuda")
+
+        def one(i):
+            pp, ss = pool[i % len(pool)]
+            w4.gemv_swiglu(xt, pp, ss, c.group, out=y)
+
+        mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+        b = c.n * c.k + 2 * c.n * (c.k // c.group) * 2 + m * c.k * 2 + m * c.n * 2
+        out[f"swiglu_{m}x5120x(2x17408)_g128"] = {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
+                                                  "gbs": b / (mean * 1e-3) / 1e9,
+                                                  "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
 
 
 def prefill_component(torch, w4, synth, args):
@@ -616,7 +645,7 @@ def main():
     if "decode" not in comps:
         # component runs without the headline (profiling passes): no JSON line contract
         for name, fn in (("np4", np4_component), ("batch16", batched_decode_component),
-                         ("prefill", prefill_component), ("moe", moe_component)):
+                         ("swiglu", swiglu_component), ("prefill", prefill_component), ("moe", moe_component)):
             if name in comps:
                 res[name] = fn(torch, w4, synth, args)
         print(json.dumps({"components": res}, default=float))
@@ -626,6 +655,8 @@ def main():
         res["np4"] = np4_component(torch, w4, synth, args)
     if "batch16" in comps:
         res["batch16"] = batched_decode_component(torch, w4, synth, args)
+    if "swiglu" in comps:
+        res["swiglu"] = swiglu_component(torch, w4, synth, args)
     if "prefill" in comps:
         res["prefill"] = prefill_component(torch, w4, synth, args)
     if "moe" in comps:

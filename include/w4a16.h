@@ -135,6 +135,20 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Fused gate/up projection of a SwiGLU feed-forward, 1 <= m <= 16 rows (the
+ * SiLU-activated gate times the up projection: the rust-inference page's
+ * "SwiGLU missing gate" item; gate and up fused in one pass as in the infr
+ * page's Linear + GatedAct fusion).  packed [2n, k/8] and scales [2n, k/group]
+ * hold 2n interleaved weight rows: row 2i is the gate row of output i, row
+ * 2i + 1 its up row.  y [m, n] = fp16(SiLU(g) * u) with g, u the fp32-accumulated
+ * products x . row^T and SiLU(g) = g / (1 + e^-g) in fp32; the 2 x m x n
+ * intermediate never leaves the chip.  Errors as w4a16_gemv (m > 16 is
+ * W4A16_ERR_SHAPE); k == 0 writes zeros.
+ */
+int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                      uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group, void* stream);
+
+/*
  * MoE grouped GEMM (the routed-expert layers of the 35B-A3B MoE model on the
  * LLM170 CUDA/W4A16 page, g32).  x [rows, k] holds one row per (token, expert)
  * pair, sorted by expert; rows offsets[e] .. offsets[e+1]-1 belong to expert e

@@ -13,9 +13,9 @@ loops).  No function here is left "parity unpinned".
 """
 
 from .reference import (GROUPS, quantize, pack, unpack, dequantize, linear, linear_rows,
-                        linear_cols, linear_loops, grouped_linear)
+                        linear_cols, linear_loops, grouped_linear, silu, swiglu_linear)
 from .check import compare, Report, ELEM_TOL, ROW_TOL
 
 __all__ = ["GROUPS", "quantize", "pack", "unpack", "dequantize", "linear", "linear_rows",
-           "linear_cols", "linear_loops", "grouped_linear", "compare", "Report",
+           "linear_cols", "linear_loops", "grouped_linear", "silu", "swiglu_linear", "compare", "Report",
            "ELEM_TOL", "ROW_TOL"]

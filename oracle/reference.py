@@ -166,3 +166,26 @@ def grouped_linear(x_sorted: np.ndarray, packed: np.ndarray, s: np.ndarray,
         if hi > lo:
             y[lo:hi] = linear(x_sorted[lo:hi], packed[e], s[e], group)
     return y
+
+
+# ---------------------------------------------------------------------------
+# Gated feed-forward input (SwiGLU): the SiLU-activated gate projection times
+# the up projection (rust-inference page, the "SwiGLU missing gate" item of
+# its bug list), with the gate and up projections fused into one pass (infr
+# page, Validated models & performance, footnote on Linear + GatedAct fusion).
+# Reading: one weight tensor of 2N interleaved rows, row 2i the gate row of
+# output i and row 2i + 1 its up row; SiLU(g) = g / (1 + e^-g).
+# ---------------------------------------------------------------------------
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g)), in fp64."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_linear(x: np.ndarray, packed: np.ndarray, s: np.ndarray, group: int) -> np.ndarray:
+    """y [M, N] = SiLU(x . Wg^T) * (x . Wu^T), Wg / Wu the even / odd rows of the [2N, K] weights."""
+    z = linear(x, packed, s, group)                          # [M, 2N] fp64
+    if z.shape[1] % 2:
+        raise ValueError("gate/up weights need an even number of rows")
+    return silu(z[:, 0::2]) * z[:, 1::2]

@@ -166,6 +166,30 @@ def test_gemm_validation():
     assert w4.lib.w4a16_gemm_workspace_bytes(8, 64, 100, 32) == 0
 
 
+def test_gemv_swiglu_validation():
+    g = w4.lib.w4a16_gemv_swiglu
+    assert g(A, A, A, A, 1, 64, 128, 64, None) == w4.ERR_GROUP
+    assert g(A, A, A, A, 1, 64, 100, 32, None) == w4.ERR_SHAPE
+    assert g(A, A, A, A, 17, 64, 128, 128, None) == w4.ERR_SHAPE    # at most 16 rows
+    assert g(A, A, A, A, 1, -64, 128, 128, None) == w4.ERR_SHAPE
+    assert g(A, A, A, None, 1, 64, 128, 128, None) == w4.ERR_NULL
+    assert g(A, None, A, A, 1, 64, 128, 128, None) == w4.ERR_NULL
+    assert g(A + 8, A, A, A, 1, 64, 128, 128, None) == w4.ERR_ALIGN
+    assert g(A, A, A, A + 2, 1, 64, 128, 128, None) == w4.ERR_ALIGN
+    assert g(A, A, A, A, 1, 1 << 21, 1 << 12, 128, None) == w4.ERR_SHAPE   # 2n rows: > 2 GiB of weights
+    assert g(None, None, None, None, 0, 64, 128, 128, None) == w4.OK
+    assert g(None, None, None, None, 1, 0, 128, 128, None) == w4.OK
+
+
+def test_interleave_rows():
+    a = np.arange(12, dtype=np.uint32).reshape(3, 4)
+    b = a + 100
+    r = w4.interleave_rows(a, b)
+    assert r.shape == (6, 4) and np.array_equal(r[0::2], a) and np.array_equal(r[1::2], b)
+    with pytest.raises(ValueError):
+        w4.interleave_rows(a, b[:2])
+
+
 def test_grouped_validation():
     g = w4.lib.w4a16_grouped_gemm
     assert g(A, A, A, A, A, 4, 16, 64, 128, 48, None) == w4.ERR_GROUP

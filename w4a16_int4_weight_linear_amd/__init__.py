@@ -49,6 +49,7 @@ SIGNATURES = {
     "w4a16_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "w4a16_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
+    "w4a16_gemv_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():
@@ -162,6 +163,29 @@ def gemm(x, packed, scales, group: int, out=None, workspace=None, stream=None):
     return out
 
 
+def interleave_rows(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """Rows of gate and up interleaved (gate row i -> 2i, up row i -> 2i + 1): the
+    weight layout of gemv_swiglu, for packed words and scales alike."""
+    gate, up = np.asarray(gate), np.asarray(up)
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    out = np.empty((2 * gate.shape[0],) + gate.shape[1:], dtype=gate.dtype)
+    out[0::2], out[1::2] = gate, up
+    return out
+
+
+def gemv_swiglu(x, packed, scales, group: int, out=None, stream=None):
+    """y [m, n] = SiLU(x . Wg^T) * (x . Wu^T), 1 <= m <= 16; packed [2n, k/8] interleaves gate/up rows."""
+    torch = _torch()
+    m, k = x.shape
+    n = packed.shape[0] // 2
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _check(lib.w4a16_gemv_swiglu(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k, group, _stream(stream)),
+           "w4a16_gemv_swiglu")
+    return out
+
+
 def grouped_gemm(x, packed, scales, offsets, group: int, out=None, stream=None):
     """MoE grouped product: rows offsets[e]..offsets[e+1] of x use expert e's weights."""
     torch = _torch()
@@ -175,4 +199,4 @@ def grouped_gemm(x, packed, scales, offsets, group: int, out=None, stream=None):
 
 
 __all__ = ["lib", "LIB_PATH", "SIGNATURES", "W4A16Error", "quantize", "pack", "unpack", "gemv", "gemm",
-           "gemm_workspace", "grouped_gemm"] + list(SIGNATURES)
+           "gemm_workspace", "grouped_gemm", "interleave_rows", "gemv_swiglu"] + list(SIGNATURES)

@@ -188,6 +188,22 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
                                       need ? workspace : nullptr, dev, st));
 }
 
+int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+                      int64_t n, int64_t k, int32_t group, void* stream) {
+  if (valid_group(group) && m > 16) return W4A16_ERR_SHAPE;
+  if (n > kMaxDim / 2) return W4A16_ERR_SHAPE;
+  // the weights have 2n rows; y has n columns (checked as part of the 2n-column bound)
+  int c = common_dense_checks(x, packed, scales, y, m, 2 * n, k, group);
+  if (c < 0) return W4A16_OK;
+  if (c != W4A16_OK) return c;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));   // SiLU(0) * 0
+  if (!w4a16::gemm_skinny_fits(5, (int)(2 * n), (int)k, dev)) return W4A16_ERR_SHAPE;
+  return status_of(w4a16::launch_swiglu_skinny(x, packed, scales, y, (int)m, (int)n, (int)k, group, dev, st));
+}
+
 int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
                        uint16_t* y, int32_t num_experts, int64_t rows, int64_t n, int64_t k, int32_t group,
                        void* stream) {

@@ -20,6 +20,10 @@
 //   the B operand.
 // * The eight waves' accumulator tiles are added in wave order in LDS
 //   (deterministic) and rounded once to fp16.
+// * The same kernel serves the fused gate/up projection of a SwiGLU feed-forward
+//   (gemv_swiglu): the epilogue applies SiLU to the gate row and multiplies by
+//   the up row before the single rounding, so the 2 x M x N intermediate never
+//   reaches HBM.
 #include <atomic>
 
 #include "device.hpp"
@@ -46,7 +50,10 @@ static_assert(kXPieces == 8, "staging assumes eight pieces per thread");
 static_assert(kLds <= 160 * 1024, "LDS");
 static_assert(kWaves * kMaxBlocks * 1024 <= kLds, "the final partial tiles reuse the LDS");
 
-template <int G, bool ALIGNED>
+// SWIGLU: the 2 n weight rows interleave gate (even) and up (odd) rows of n
+// outputs; workgroup ranges are whole pairs and the epilogue writes
+// y[m, i] = SiLU(gate_i) * up_i (fp32, rounded once) instead of both rows.
+template <int G, bool ALIGNED, bool SWIGLU>
 __global__ void __launch_bounds__(kThreads)
 gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                    const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
@@ -58,9 +65,11 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
   const int lq = lane >> 4;
   const int li = lane & 15;
 
+  // rows_base / rows_extra count whole rows, or whole (gate, up) row pairs
+  constexpr int kUnit = SWIGLU ? 2 : 1;
   const int blk = blockIdx.x;
-  const int nr = rows_base + (blk < rows_extra ? 1 : 0);
-  const int r0 = blk * rows_base + (blk < rows_extra ? blk : rows_extra);
+  const int nr = kUnit * (rows_base + (blk < rows_extra ? 1 : 0));
+  const int r0 = kUnit * (blk * rows_base + (blk < rows_extra ? blk : rows_extra));
   const int nb = (nr + 15) >> 4;                   // <= kMaxBlocks (the host sizes the grid)
   const int lines = (K + KL - 1) / KL;
   const int chunks = (lines + kChunkLines - 1) / kChunkLines;
@@ -172,6 +181,7 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
   const uint32_t sel_lq = (uint32_t)(2 * lq) * 0x00010001u + (uint32_t)(2 * lq + 1) * 0x01000100u;
   const uint8_t* xfrag = smem + li * kXPitch + 64 * lq;
 
+  // One unit in flight per wave (a second one measured no faster).
   for (int c = 0; c < chunks; ++c) {
     const int cu = chunk_units(c);
     const uint8_t* xc = xfrag + (c & 1) * kXBuf;
@@ -231,21 +241,60 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
     f32x4 t = red[wave * 64 + lane];
     for (int w = 1; w < kWaves; ++w) t += red[(w * kMaxBlocks + wave) * 64 + lane];
     // lane holds weight rows 4 lq .. 4 lq + 3 of block `wave` for activation row li
+    if constexpr (SWIGLU) {
+      // rows r0 + rr (gate) and r0 + rr + 1 (up) for even rr: output (r0 + rr) / 2
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = 16 * wave + 4 * lq + j;
-      if (rr < nr) y[(size_t)li * N + r0 + rr] = float_to_half_bits(t[j]);
+      for (int j = 0; j < 4; j += 2) {
+        const int rr = 16 * wave + 4 * lq + j;
+        if (rr < nr) {
+          const float g = t[j];
+          const float v = g / (1.0f + __expf(-g)) * t[j + 1];
+          y[(size_t)li * (N >> 1) + ((r0 + rr) >> 1)] = float_to_half_bits(v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 16 * wave + 4 * lq + j;
+        if (rr < nr) y[(size_t)li * N + r0 + rr] = float_to_half_bits(t[j]);
+      }
     }
   }
 }
 
-template <int G, bool ALIGNED>
+template <int G, bool ALIGNED, bool SWIGLU>
 hipError_t launch_ga(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m, int n,
-                     int k, int blocks, hipStream_t stream) {
+                     int k, int blocks, int units, hipStream_t stream) {
   (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL((gemm_skinny_kernel<G, ALIGNED>), dim3(blocks), dim3(kThreads), 0, stream, x, packed, scales,
-                     y, m, n, k, n / blocks, n % blocks);
+  hipLaunchKernelGGL((gemm_skinny_kernel<G, ALIGNED, SWIGLU>), dim3(blocks), dim3(kThreads), 0, stream, x, packed,
+                     scales, y, m, n, k, units / blocks, units % blocks);
   return hipGetLastError();
+}
+
+// n weight rows in units of `unit` rows (2: gate/up pairs); returns the grid.
+int skinny_grid(int n, int unit, const DeviceInfo& dev) {
+  // One workgroup per CU (the LDS allows no more), more if a range would exceed
+  // kMaxBlocks row blocks; at least 16 rows per workgroup.
+  const int units = n / unit;
+  const int lo = 16 / unit, hi = 16 * kMaxBlocks / unit;
+  int g = dev.num_cu;
+  if ((int64_t)g * lo > units) g = (units + lo - 1) / lo;
+  if ((int64_t)g * hi < units) g = (units + hi - 1) / hi;
+  return g;
+}
+
+template <bool SWIGLU>
+hipError_t launch_s(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m, int n,
+                    int k, int group, const DeviceInfo& dev, hipStream_t stream) {
+  const int unit = SWIGLU ? 2 : 1;
+  const int g = skinny_grid(n, unit, dev);
+  const int units = n / unit;
+  const int spr = k / group;
+  if (group == 32)
+    return spr % 8 == 0 ? launch_ga<32, true, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream)
+                        : launch_ga<32, false, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream);
+  return spr % 2 == 0 ? launch_ga<128, true, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream)
+                      : launch_ga<128, false, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream);
 }
 
 }  // namespace
@@ -258,18 +307,12 @@ bool gemm_skinny_fits(int m, int n, int k, const DeviceInfo& dev) {
 
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                               int n, int k, int group, const DeviceInfo& dev, hipStream_t stream) {
-  // One workgroup per CU (the LDS allows no more), more if a range would exceed
-  // kMaxBlocks row blocks; at least 16 rows per workgroup.
-  int g = dev.num_cu;
-  if ((int64_t)g * 16 > n) g = (n + 15) / 16;
-  const int per = 16 * kMaxBlocks;
-  if ((int64_t)g * per < n) g = (n + per - 1) / per;
-  const int spr = k / group;
-  if (group == 32)
-    return spr % 8 == 0 ? launch_ga<32, true>(x, packed, scales, y, m, n, k, g, stream)
-                        : launch_ga<32, false>(x, packed, scales, y, m, n, k, g, stream);
-  return spr % 2 == 0 ? launch_ga<128, true>(x, packed, scales, y, m, n, k, g, stream)
-                      : launch_ga<128, false>(x, packed, scales, y, m, n, k, g, stream);
+  return launch_s<false>(x, packed, scales, y, m, n, k, group, dev, stream);
+}
+
+hipError_t launch_swiglu_skinny(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
+                                int m, int n_out, int k, int group, const DeviceInfo& dev, hipStream_t stream) {
+  return launch_s<true>(x, packed, scales, y, m, 2 * n_out, k, group, dev, stream);
 }
 
 }  // namespace w4a16

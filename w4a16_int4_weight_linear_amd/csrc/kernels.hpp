@@ -44,6 +44,9 @@ hipError_t launch_gemv_mfma(const uint16_t* x, const uint32_t* packed, const uin
 bool gemm_skinny_fits(int m, int n, int k, const DeviceInfo& dev);
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                               int n, int k, int group, const DeviceInfo& dev, hipStream_t stream);
+// y [m, n_out] = SiLU(gate) * up, packed/scales holding 2 n_out interleaved rows (1 <= m <= 16).
+hipError_t launch_swiglu_skinny(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
+                                int m, int n_out, int k, int group, const DeviceInfo& dev, hipStream_t stream);
 
 // ---- prefill GEMM (gemm.hip) ----
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int group, const DeviceInfo& dev);
