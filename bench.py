@@ -458,10 +458,13 @@ def trace_summary(trace_csv, command):
     labels = {"gemm_kernel": ["M=512", "M=4096"],
               "gemv_kernel<1>": ["one of up 5120->17408 / down 17408->5120 (same bytes)"],
               "gemv_mfma_kernel<4": ["N=5120", "N=17408"],
+              "gemm_skinny_kernel<128, true, true>": ["M=1, gate+up 5120->2x17408 (SwiGLU)",
+                                                      "M=4, gate+up 5120->2x17408 (SwiGLU)"],
               "gemm_skinny_kernel": ["M=16, up 5120->17408 (batched decode)"],
               "grouped_gemm_kernel": ["256 experts x [512 x 2048] g32, 4096 routed rows, uniform top-8",
                                       "same bank, Zipf-skewed top-8 (244 experts used)"]}
     files = {"gemv_kernel<1>": "gemv_m1_decode_27b_ffn", "gemv_mfma_kernel<4": "gemv_m4_np4_27b_ffn",
+             "gemm_skinny_kernel<128, true, true>": "swiglu_gate_up_27b",
              "gemm_skinny_kernel": "gemm_skinny_m16_27b_up",
              "gemm_kernel": "gemm_prefill_27b_ffn", "grouped_gemm_kernel": "grouped_gemm_moe_256e"}
     groups = defaultdict(list)
