@@ -481,11 +481,19 @@ def trace_summary(trace_csv, command):
     def clusters(d, n):
         # The benchmark runs its workloads one after another: split the launches,
         # in time order, at the n - 1 largest pauses between consecutive starts.
+        # Each workload is a sizeable run (a warm-up launch alone before a graph
+        # capture pause is not one): every segment keeps >= 1/(4 n) of the launches.
         d = sorted(d)
         if n <= 1 or len(d) < 2:
             return [sorted(t for _, t in d)]
-        gaps = sorted(range(1, len(d)), key=lambda i: d[i][0] - d[i - 1][0], reverse=True)[: n - 1]
-        cuts = [0] + sorted(gaps) + [len(d)]
+        least = max(1, len(d) // (4 * n))
+        cuts = [0, len(d)]
+        for i in sorted(range(1, len(d)), key=lambda i: d[i][0] - d[i - 1][0], reverse=True):
+            if len(cuts) == n + 1:
+                break
+            trial = sorted(cuts + [i])
+            if all(trial[j + 1] - trial[j] >= least for j in range(len(trial) - 1)):
+                cuts = trial
         return [sorted(t for _, t in d[cuts[i]:cuts[i + 1]]) for i in range(len(cuts) - 1)]
 
     out = defaultdict(list)
