@@ -163,6 +163,43 @@ int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
                        const int32_t* offsets, uint16_t* y, int32_t num_experts,
                        int64_t rows, int64_t n, int64_t k, int32_t group, void* stream);
 
+/*
+ * The routed-expert (MoE) steps either side of the grouped product, for the
+ * 35B-A3B MoE layers of the LLM170 / infr pages (the MoE tiles and the batched
+ * MoE path; the step around expert_gateup / expert_down).  All pointers are
+ * device pointers; nothing synchronises.
+ *
+ * w4a16_moe_route: topk_ids int32 [tokens, topk] (expert of each (token, slot)
+ * pair) -> offsets int32 [num_experts + 1] (rows of expert e are offsets[e] ..
+ * offsets[e+1]-1), pair_token int32 [tokens * topk] (token of each grouped row)
+ * and pair_row int32 [tokens, topk] (grouped row of each pair).  The order of
+ * rows inside one expert is unspecified (it changes no product or combined
+ * output).  An id outside [0, num_experts) gets pair_row = -1 and no row; then
+ * offsets[num_experts] < tokens * topk.  1 <= num_experts <= 32768.
+ */
+int w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts,
+                    int32_t* offsets, int32_t* pair_token, int32_t* pair_row, void* stream);
+
+/*
+ * w4a16_grouped_gemm with the activations gathered: x [tokens, k] holds the
+ * token rows unsorted and grouped row r reads x[pair_token[r]] (pair_token from
+ * w4a16_moe_route), so no expert-sorted copy of x is made.  y [rows, n] as in
+ * w4a16_grouped_gemm.  A pair_token outside [0, tokens) reads zeros.
+ */
+int w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
+                              const uint16_t* scales, const int32_t* offsets, uint16_t* y,
+                              int32_t num_experts, int64_t rows, int64_t tokens, int64_t n, int64_t k,
+                              int32_t group, void* stream);
+
+/*
+ * Router-weighted combine: out [tokens, n] fp16, out[t] = sum over slots j (in
+ * order) of weights[t, j] * y_pairs[pair_row[t, j]], accumulated in fp32 and
+ * rounded once.  y_pairs [rows, n] fp16 (the grouped product), weights fp32
+ * [tokens, topk].  A pair_row outside [0, rows) contributes nothing.
+ */
+int w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
+                      int64_t tokens, int32_t topk, int64_t rows, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,9 +13,11 @@ loops).  No function here is left "parity unpinned".
 """
 
 from .reference import (GROUPS, quantize, pack, unpack, dequantize, linear, linear_rows,
-                        linear_cols, linear_loops, grouped_linear, silu, swiglu_linear)
+                        linear_cols, linear_loops, grouped_linear, silu, swiglu_linear, moe_route,
+                        moe_combine, moe_layer)
 from .check import compare, Report, ELEM_TOL, ROW_TOL
 
 __all__ = ["GROUPS", "quantize", "pack", "unpack", "dequantize", "linear", "linear_rows",
-           "linear_cols", "linear_loops", "grouped_linear", "silu", "swiglu_linear", "compare", "Report",
+           "linear_cols", "linear_loops", "grouped_linear", "silu", "swiglu_linear", "moe_route", "moe_combine", "moe_layer",
+           "compare", "Report",
            "ELEM_TOL", "ROW_TOL"]

@@ -189,3 +189,63 @@ def swiglu_linear(x: np.ndarray, packed: np.ndarray, s: np.ndarray, group: int) 
     if z.shape[1] % 2:
         raise ValueError("gate/up weights need an even number of rows")
     return silu(z[:, 0::2]) * z[:, 1::2]
+
+
+# ---------------------------------------------------------------------------
+# The routed-expert (MoE) layer around the grouped product: routing each token
+# to its top-k experts, the experts' products, and the router-weighted combine
+# back into one output row per token (the MoE tiles and the batched MoE path of
+# the LLM170 / infr pages; the step either side of expert_gateup/expert_down).
+# Readings: expert ids arrive as an int [T, topk] array; the grouped rows are
+# ordered by (expert, token, slot); the combine is sum_j w[t, j] * y_pair(t, j)
+# with the router weights w given (fp32), accumulated in fp64 here.
+# ---------------------------------------------------------------------------
+def moe_route(topk_ids: np.ndarray, experts: int):
+    """(offsets int64 [E+1], pair_token int64 [P], pair_slot int64 [P], pair_row int64 [T, topk]).
+
+    Sorted rows r = 0 .. P-1 list the (token, slot) pairs by (expert, token, slot);
+    rows offsets[e] .. offsets[e+1]-1 belong to expert e; pair_row[t, j] is the row of (t, j).
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    if ids.ndim != 2 or np.any(ids < 0) or np.any(ids >= experts):
+        raise ValueError("expert ids must be an int [T, topk] array in [0, experts)")
+    t_count, topk = ids.shape
+    pairs = [(int(ids[t, j]), t, j) for t in range(t_count) for j in range(topk)]
+    pairs.sort()
+    offsets = np.zeros(experts + 1, dtype=np.int64)
+    for e, _, _ in pairs:
+        offsets[e + 1] += 1
+    offsets = np.cumsum(offsets)
+    pair_token = np.array([t for _, t, _ in pairs], dtype=np.int64)
+    pair_slot = np.array([j for _, _, j in pairs], dtype=np.int64)
+    pair_row = np.zeros((t_count, topk), dtype=np.int64)
+    for r, (_, t, j) in enumerate(pairs):
+        pair_row[t, j] = r
+    return offsets, pair_token, pair_slot, pair_row
+
+
+def moe_combine(y_pairs: np.ndarray, pair_row: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """out [T, N] = sum_j weights[t, j] * y_pairs[pair_row[t, j]], in fp64."""
+    y_pairs = np.asarray(y_pairs, dtype=np.float64)
+    w = np.asarray(weights, dtype=np.float64)
+    t_count, topk = w.shape
+    out = np.zeros((t_count, y_pairs.shape[1]), dtype=np.float64)
+    for t in range(t_count):
+        for j in range(topk):
+            out[t] += w[t, j] * y_pairs[pair_row[t, j]]
+    return out
+
+
+def moe_layer(x: np.ndarray, topk_ids: np.ndarray, weights: np.ndarray, packed: np.ndarray, s: np.ndarray,
+              group: int) -> np.ndarray:
+    """The routed-expert layer by its definition: out[t] = sum_j w[t, j] * (x[t] . W_{e(t, j)}^T), fp64."""
+    x = np.asarray(x, dtype=np.float16)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.float64)
+    out = np.zeros((x.shape[0], packed.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        ts, js = np.nonzero(ids == e)
+        ye = linear(x[ts], packed[e], s[e], group)          # [pairs of e, N]
+        for r in range(len(ts)):
+            out[ts[r]] += w[ts[r], js[r]] * ye[r]
+    return out

@@ -105,6 +105,7 @@ class Routing:
     pair_token: np.ndarray
     offsets: np.ndarray
     counts: np.ndarray = field(default=None)
+    choice: np.ndarray = field(default=None)   # the draws themselves: expert of (token, slot), [tokens, topk]
 
 
 def route_uniform(rng: np.random.Generator, tokens: int, experts: int, topk: int) -> Routing:
@@ -129,7 +130,15 @@ def _sorted_pairs(choice: np.ndarray, experts: int) -> Routing:
     e, t = e[order], t[order]
     counts = np.bincount(e, minlength=experts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    return Routing(e.astype(np.int32), t.astype(np.int32), offsets, counts)
+    return Routing(e.astype(np.int32), t.astype(np.int32), offsets, counts, choice.astype(np.int32))
+
+
+def router_weights(rng: np.random.Generator, tokens: int, topk: int) -> np.ndarray:
+    """fp32 [tokens, topk] positive weights summing to 1 per token: a softmax over
+    N(0, 1) logits, standing in for a router's top-k probabilities."""
+    z = rng.standard_normal((tokens, topk))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 def moe_inputs(case: MoECase, experts: int | None = None):

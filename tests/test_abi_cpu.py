@@ -181,6 +181,28 @@ def test_gemv_swiglu_validation():
     assert g(None, None, None, None, 1, 0, 128, 128, None) == w4.OK
 
 
+def test_moe_validation():
+    r = w4.lib.w4a16_moe_route
+    assert r(A, 4, 0, 8, A, A, A, None) == w4.ERR_SHAPE          # topk >= 1
+    assert r(A, 4, 2, 0, A, A, A, None) == w4.ERR_SHAPE          # at least one expert
+    assert r(A, 4, 2, 40000, A, A, A, None) == w4.ERR_SHAPE      # counted in LDS
+    assert r(A, -1, 2, 8, A, A, A, None) == w4.ERR_SHAPE
+    assert r(A, 4, 2, 8, None, A, A, None) == w4.ERR_NULL
+    assert r(None, 4, 2, 8, A, A, A, None) == w4.ERR_NULL
+    assert r(A + 2, 4, 2, 8, A, A, A, None) == w4.ERR_ALIGN
+    gg = w4.lib.w4a16_grouped_gemm_gather
+    assert gg(A, A, A, A, A, A, 4, 16, 8, 64, 128, 48, None) == w4.ERR_GROUP
+    assert gg(A, None, A, A, A, A, 4, 16, 8, 64, 128, 32, None) == w4.ERR_NULL
+    assert gg(A, A + 2, A, A, A, A, 4, 16, 8, 64, 128, 32, None) == w4.ERR_ALIGN
+    assert gg(A, A, A, A, A, A, 4, 16, -8, 64, 128, 32, None) == w4.ERR_SHAPE
+    assert gg(None, None, None, None, None, None, 4, 0, 8, 64, 128, 32, None) == w4.OK
+    c = w4.lib.w4a16_moe_combine
+    assert c(A, A, A, A, 4, 0, 32, 64, None) == w4.ERR_SHAPE
+    assert c(A, A, A, None, 4, 2, 32, 64, None) == w4.ERR_NULL
+    assert c(A, A, A, A + 8, 4, 2, 32, 64, None) == w4.ERR_ALIGN
+    assert c(None, None, None, None, 0, 2, 0, 64, None) == w4.OK
+
+
 def test_interleave_rows():
     a = np.arange(12, dtype=np.uint32).reshape(3, 4)
     b = a + 100

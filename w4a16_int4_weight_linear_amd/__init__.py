@@ -50,6 +50,10 @@ SIGNATURES = {
     "w4a16_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_gemv_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
+    "w4a16_moe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "w4a16_grouped_gemm_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i32,
+                                                 _vp]),
+    "w4a16_moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():
@@ -198,5 +202,45 @@ def grouped_gemm(x, packed, scales, offsets, group: int, out=None, stream=None):
     return out
 
 
+def moe_route(topk_ids, experts: int, stream=None):
+    """Device routing of int32 topk_ids [tokens, topk] -> (offsets [E+1], pair_token [P], pair_row [tokens, topk])."""
+    torch = _torch()
+    t, topk = topk_ids.shape
+    dev_ = topk_ids.device
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device=dev_)
+    pair_token = torch.empty(t * topk, dtype=torch.int32, device=dev_)
+    pair_row = torch.empty((t, topk), dtype=torch.int32, device=dev_)
+    _check(lib.w4a16_moe_route(_ptr(topk_ids), t, topk, experts, _ptr(offsets), _ptr(pair_token), _ptr(pair_row),
+                               _stream(stream)), "w4a16_moe_route")
+    return offsets, pair_token, pair_row
+
+
+def grouped_gemm_gather(x, pair_token, packed, scales, offsets, group: int, out=None, stream=None):
+    """Grouped product whose row r reads token pair_token[r] of x [tokens, k]."""
+    torch = _torch()
+    tokens, k = x.shape
+    rows = pair_token.shape[0]
+    experts, n = packed.shape[0], packed.shape[1]
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.float16, device=x.device)
+    _check(lib.w4a16_grouped_gemm_gather(_ptr(x), _ptr(pair_token), _ptr(packed), _ptr(scales), _ptr(offsets),
+                                         _ptr(out), experts, rows, tokens, n, k, group, _stream(stream)),
+           "w4a16_grouped_gemm_gather")
+    return out
+
+
+def moe_combine(y_pairs, pair_row, weights, out=None, stream=None):
+    """out [tokens, n] = sum_j weights[t, j] * y_pairs[pair_row[t, j]] (weights fp32 [tokens, topk])."""
+    torch = _torch()
+    tokens, topk = pair_row.shape
+    rows, n = y_pairs.shape
+    if out is None:
+        out = torch.empty((tokens, n), dtype=torch.float16, device=y_pairs.device)
+    _check(lib.w4a16_moe_combine(_ptr(y_pairs), _ptr(pair_row), _ptr(weights), _ptr(out), tokens, topk, rows, n,
+                                 _stream(stream)), "w4a16_moe_combine")
+    return out
+
+
 __all__ = ["lib", "LIB_PATH", "SIGNATURES", "W4A16Error", "quantize", "pack", "unpack", "gemv", "gemm",
-           "gemm_workspace", "grouped_gemm", "interleave_rows", "gemv_swiglu"] + list(SIGNATURES)
+           "gemm_workspace", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
+           "grouped_gemm_gather", "moe_combine"] + list(SIGNATURES)

@@ -56,6 +56,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // offsets below 2^31 (an offset of 2^31 marks an out-of-range load).
 constexpr int64_t kMaxBufferBytes = (int64_t)1 << 31;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// Experts the routing kernel counts in LDS (one int per expert beside 4 KB).
+constexpr int32_t kMaxRouteExperts = 32768;
 
 int common_dense_checks(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
                         int64_t m, int64_t n, int64_t k, int32_t group) {
@@ -225,6 +227,60 @@ int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(rows * n), st));
   return status_of(w4a16::launch_grouped_gemm(x, packed, scales, offsets, y, num_experts, (int)rows, (int)n,
                                               (int)k, group, dev, st));
+}
+
+int w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
+                              const uint16_t* scales, const int32_t* offsets, uint16_t* y, int32_t num_experts,
+                              int64_t rows, int64_t tokens, int64_t n, int64_t k, int32_t group, void* stream) {
+  if (!valid_group(group)) return W4A16_ERR_GROUP;
+  if (num_experts < 0 || rows < 0 || tokens < 0 || n < 0 || k < 0 || k % group) return W4A16_ERR_SHAPE;
+  if (rows > kMaxDim || tokens > kMaxDim || n > kMaxDim || k > kMaxDim) return W4A16_ERR_SHAPE;
+  if (rows == 0 || n == 0) return W4A16_OK;
+  if (num_experts == 0) return W4A16_ERR_SHAPE;
+  if (!y || !offsets) return W4A16_ERR_NULL;
+  if (k > 0 && (!x || !packed || !scales || !pair_token)) return W4A16_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(offsets, 4) ||
+      (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(pair_token, 4))))
+    return W4A16_ERR_ALIGN;
+  if ((int64_t)num_experts * n * (k / 2) >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (2 * tokens * k >= kMaxBufferBytes || 2 * rows * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(rows * n), st));
+  return status_of(w4a16::launch_grouped_gemm_gather(x, pair_token, (int)tokens, packed, scales, offsets, y,
+                                                     num_experts, (int)rows, (int)n, (int)k, group, dev, st));
+}
+
+int w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts, int32_t* offsets,
+                    int32_t* pair_token, int32_t* pair_row, void* stream) {
+  if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > kMaxRouteExperts) return W4A16_ERR_SHAPE;
+  if (tokens * topk >= ((int64_t)1 << 31)) return W4A16_ERR_SHAPE;
+  if (!offsets) return W4A16_ERR_NULL;
+  if (tokens > 0 && (!topk_ids || !pair_token || !pair_row)) return W4A16_ERR_NULL;
+  if (!aligned(offsets, 4) || (tokens > 0 && (!aligned(topk_ids, 4) || !aligned(pair_token, 4) ||
+                                              !aligned(pair_row, 4))))
+    return W4A16_ERR_ALIGN;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  if (w4a16::moe_route_lds(num_experts) > dev.max_lds) return W4A16_ERR_SHAPE;
+  return status_of(w4a16::launch_moe_route(topk_ids, (int)(tokens * topk), topk, num_experts, offsets, pair_token,
+                                           pair_row, dev, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
+                      int64_t tokens, int32_t topk, int64_t rows, int64_t n, void* stream) {
+  if (tokens < 0 || topk < 1 || rows < 0 || n < 0) return W4A16_ERR_SHAPE;
+  if (tokens > kMaxDim || rows > kMaxDim || n > kMaxDim || tokens * topk >= ((int64_t)1 << 31)) return W4A16_ERR_SHAPE;
+  if (2 * rows * n >= kMaxBufferBytes || 2 * tokens * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (tokens == 0 || n == 0) return W4A16_OK;
+  if (!out || !pair_row || !weights || (rows > 0 && !y_pairs)) return W4A16_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(pair_row, 4) || !aligned(weights, 4) || (rows > 0 && !aligned(y_pairs, 16)))
+    return W4A16_ERR_ALIGN;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  return status_of(w4a16::launch_moe_combine(y_pairs, pair_row, weights, out, (int)tokens, topk, (int)n, (int)rows,
+                                             reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

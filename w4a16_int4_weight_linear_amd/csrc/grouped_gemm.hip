@@ -30,6 +30,9 @@
 // * The weights are the MFMA's A operand (v_mfma_f32_16x16x32_f16, 16 columns
 //   x 32 k) and the activations its B operand, so a lane ends with four
 //   consecutive output columns of one row: 8-byte stores.
+// * Gather variant (launch_grouped_gemm_gather): row r's activations are read
+//   from token pair_token[r] of the unsorted token rows, so the expert-sorted
+//   copy of the activations is never written.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "mfma_operands.hpp"
@@ -136,7 +139,8 @@ __device__ inline f16x2 pick_scale(uint32_t lo, uint32_t hi, uint32_t sel) {
 template <int G, bool ALIGNED, int MB>
 __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed_e,
                                           const uint16_t* __restrict__ scales_e, uint16_t* __restrict__ y,
-                                          int N, int K, int rows_total, const Item& it, int band, uint8_t* lds) {
+                                          int N, int K, int rows_total, const Item& it, int band, uint8_t* lds,
+                                          const int32_t* __restrict__ pair_token, int x_rows) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,7 +153,7 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed_e, (uint32_t)N * row_w);
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales_e, (uint32_t)N * spr * 2u);
   const uint32_t kbytes = (uint32_t)K * 2u;
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)rows_total * kbytes);
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)x_rows * kbytes);
   const int steps = (K + KS - 1) / KS;
 
   // ---- whole-line weight loads: instruction i of block b reads rows 8 i .. 8 i + 7 ----
@@ -207,7 +211,11 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
   const int xr = tid / kRowThreads;
   const int xp = tid % kRowThreads;
   const bool xrow_ok = xr < it.rows;
-  const uint32_t xrow_off = (uint32_t)(it.row_begin + xr) * kbytes;
+  // gather: row r of the grouped product is token pair_token[r] of x (a token
+  // outside x reads zero through the descriptor's range check)
+  const int grow = it.row_begin + xr;
+  const uint32_t xsrc = (pair_token && xrow_ok && grow < rows_total) ? (uint32_t)pair_token[grow] : (uint32_t)grow;
+  const uint32_t xrow_off = xsrc < (uint32_t)x_rows ? xsrc * kbytes : kOutOfRange;
   auto load_x = [&](int s, u32x4 (&v)[kXPieces]) {
 #pragma unroll
     for (int p = 0; p < kXPieces; ++p) {
@@ -348,7 +356,8 @@ template <int G, bool ALIGNED>
 __global__ void __launch_bounds__(kThreads)
 grouped_gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                     const uint16_t* __restrict__ scales, const int32_t* __restrict__ offsets,
-                    uint16_t* __restrict__ y, int experts, int N, int K, int rows_total, int bands) {
+                    uint16_t* __restrict__ y, int experts, int N, int K, int rows_total, int bands,
+                    const int32_t* __restrict__ pair_token, int x_rows) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
 
   // Consecutive workgroup ids go to different XCDs (round robin over 8): the
@@ -364,16 +373,18 @@ grouped_gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__
   const uint32_t* pe = packed + e * (size_t)N * (size_t)(K >> 3);
   const uint16_t* se = scales + e * (size_t)N * (size_t)(K / G);
   if (it.rows > 16)
-    item_body<G, ALIGNED, 2>(x, pe, se, y, N, K, rows_total, it, band, lds);
+    item_body<G, ALIGNED, 2>(x, pe, se, y, N, K, rows_total, it, band, lds, pair_token, x_rows);
   else
-    item_body<G, ALIGNED, 1>(x, pe, se, y, N, K, rows_total, it, band, lds);
+    item_body<G, ALIGNED, 1>(x, pe, se, y, N, K, rows_total, it, band, lds, pair_token, x_rows);
 }
 
 }  // namespace
 
-hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
-                               const int32_t* offsets, uint16_t* y, int experts, int rows, int n, int k,
-                               int group, const DeviceInfo&, hipStream_t stream) {
+namespace {
+
+hipError_t launch_grouped(const uint16_t* x, const int32_t* pair_token, int x_rows, const uint32_t* packed,
+                          const uint16_t* scales, const int32_t* offsets, uint16_t* y, int experts, int rows, int n,
+                          int k, int group, hipStream_t stream) {
   const int bands = (n + BN - 1) / BN;
   // sum over experts of ceil(r_e / RB) <= experts + ceil(rows / RB); rounded up to whole XCD rounds
   const int64_t items = ((int64_t)experts + (rows + RB - 1) / RB + 7) / 8 * 8;
@@ -382,22 +393,26 @@ hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const 
   const int spr = k / group;
   (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (group == 32) {
-    if (spr % 8 == 0)
-      hipLaunchKernelGGL((grouped_gemm_kernel<32, true>), grid, block, 0, stream, x, packed, scales, offsets, y,
-                         experts, n, k, rows, bands);
-    else
-      hipLaunchKernelGGL((grouped_gemm_kernel<32, false>), grid, block, 0, stream, x, packed, scales, offsets, y,
-                         experts, n, k, rows, bands);
-  } else {
-    if (spr % 2 == 0)
-      hipLaunchKernelGGL((grouped_gemm_kernel<128, true>), grid, block, 0, stream, x, packed, scales, offsets, y,
-                         experts, n, k, rows, bands);
-    else
-      hipLaunchKernelGGL((grouped_gemm_kernel<128, false>), grid, block, 0, stream, x, packed, scales, offsets, y,
-                         experts, n, k, rows, bands);
-  }
+  auto kern = group == 32 ? (spr % 8 == 0 ? grouped_gemm_kernel<32, true> : grouped_gemm_kernel<32, false>)
+                          : (spr % 2 == 0 ? grouped_gemm_kernel<128, true> : grouped_gemm_kernel<128, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, x, packed, scales, offsets, y, experts, n, k, rows, bands,
+                     pair_token, x_rows);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                               const int32_t* offsets, uint16_t* y, int experts, int rows, int n, int k,
+                               int group, const DeviceInfo&, hipStream_t stream) {
+  return launch_grouped(x, nullptr, rows, packed, scales, offsets, y, experts, rows, n, k, group, stream);
+}
+
+hipError_t launch_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, int tokens,
+                                      const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
+                                      uint16_t* y, int experts, int rows, int n, int k, int group,
+                                      const DeviceInfo&, hipStream_t stream) {
+  return launch_grouped(x, pair_token, tokens, packed, scales, offsets, y, experts, rows, n, k, group, stream);
 }
 
 }  // namespace w4a16

@@ -59,6 +59,19 @@ hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const 
                                const int32_t* offsets, uint16_t* y, int experts, int rows, int n, int k,
                                int group, const DeviceInfo& dev, hipStream_t stream);
 
+// Gather variant: row r of the product reads row pair_token[r] of x [tokens, k].
+hipError_t launch_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, int tokens,
+                                      const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
+                                      uint16_t* y, int experts, int rows, int n, int k, int group,
+                                      const DeviceInfo& dev, hipStream_t stream);
+
+// ---- MoE routing and combine (moe.hip) ----
+size_t moe_route_lds(int experts);
+hipError_t launch_moe_route(const int32_t* ids, int pairs, int topk, int experts, int32_t* offsets,
+                            int32_t* pair_token, int32_t* pair_row, const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
+                              int tokens, int topk, int n, int rows, hipStream_t stream);
+
 // ---- y = 0 (the empty sum, k == 0) ----
 hipError_t launch_zero_fill(uint16_t* y, size_t count, hipStream_t stream);
 
