@@ -367,12 +367,38 @@ def moe_component(torch, w4, synth, args):
         w4.grouped_gemm(xs2, pp, ss, offs2, c.group, out=y)
 
     mean2, _ = per_launch(torch, one_skewed, args.steps, graph=True, outputs=(y,))
+    # Not graded: the whole routed-expert layer on the same bank (route on the
+    # device, gathered grouped product, router-weighted combine of 512 tokens).
+    ids_t = torch.from_numpy(r.choice).to("cuda")
+    xt = torch.from_numpy(x).to("cuda")
+    wts = torch.from_numpy(synth.router_weights(np.random.default_rng(c.seed + 500), c.tokens, c.topk)).to("cuda")
+    offs_l = torch.empty(c.experts + 1, dtype=torch.int32, device="cuda")
+    tok_l = torch.empty(rows, dtype=torch.int32, device="cuda")
+    row_l = torch.empty((c.tokens, c.topk), dtype=torch.int32, device="cuda")
+    out_l = torch.empty((c.tokens, c.n), dtype=torch.float16, device="cuda")
+
+    def layer(i):
+        pp, ss = pool[i % len(pool)]
+        w4.lib.w4a16_moe_route(w4._ptr(ids_t), c.tokens, c.topk, c.experts, w4._ptr(offs_l), w4._ptr(tok_l),
+                               w4._ptr(row_l), w4._stream(None))
+        w4.grouped_gemm_gather(xt, tok_l, pp, ss, offs_l, c.group, out=y)
+        w4.moe_combine(y, row_l, wts, out=out_l)
+
+    def gather_only(i):
+        pp, ss = pool[i % len(pool)]
+        w4.grouped_gemm_gather(xt, tok_l, pp, ss, offs_l, c.group, out=y)
+
+    mean3, _ = per_launch(torch, layer, args.steps, graph=True, outputs=(out_l,))
+    mean4, _ = per_launch(torch, gather_only, args.steps, graph=True, outputs=(y,))
+    b_gather = b - rows * c.k * 2 + c.tokens * c.k * 2 + rows * 4
     used = int(np.count_nonzero(rs.counts))
     b2 = used * (c.n * c.k // 2 + c.n * (c.k // c.group) * 2) + rows * c.k * 2 + rows * c.n * 2 + (c.experts + 1) * 4
     return {"launch_ms": mean, "launch_ms_median": med, "bytes": b, "gbs": b / (mean * 1e-3) / 1e9,
             "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, "tflops": fl / (mean * 1e-3) / 1e12,
             "skewed_routing": {"experts_used": used, "max_rows": int(rs.counts.max()), "launch_ms": mean2,
-                               "bytes": b2, "gbs": b2 / (mean2 * 1e-3) / 1e9}}
+                               "bytes": b2, "gbs": b2 / (mean2 * 1e-3) / 1e9},
+            "gathered": {"launch_ms": mean4, "bytes": b_gather, "gbs": b_gather / (mean4 * 1e-3) / 1e9},
+            "layer_route_gather_combine": {"ms": mean3, "tokens": c.tokens}}
 
 
 def traffic_probe(torch, w4, synth):
