@@ -28,10 +28,17 @@ def manifest():
                   "recipe": "per-expert fp32 weights e = 0..E-1, then fp16 x [tokens, k], then for each token in "
                             "order topk distinct experts uniformly; pairs sorted by (expert, token)"}
            for name, c in synth.MOE_CASES.items()}
+    extra = {
+        "batched_decode_m16": "weights of gemv_np4_4x5120x17408_g128; x fp16 [16, 5120] from default_rng(seed + 100)",
+        "swiglu_gate_up": "gate then up fp32 weights [17408, 5120] from default_rng(seed of gemv_up_1x5120x17408_g128 "
+                          "+ 200), rows interleaved (gate 2i, up 2i + 1); x [m, 5120] from the same generator",
+        "moe_router_weights": "softmax over N(0, 1) logits [tokens, topk] from default_rng(moe seed + 500), fp32",
+    }
     return {
         "generator": "numpy.random.default_rng(seed) (PCG64)",
         "dense": dense,
         "moe": moe,
+        "other_workloads": extra,
         "parity": {
             "floating_point": {"elementwise": f"|y - y_ref| <= {oracle.ELEM_TOL} * max|y_ref|",
                                "per_row": f"||y_row - y_ref_row||_2 <= {oracle.ROW_TOL} * ||y_ref_row||_2",
@@ -39,7 +46,8 @@ def manifest():
                                             "for comparison only where stated"},
             "bit_exact": "integer activations in [-2, 2], codes in [-8, 7], power-of-two scales: every sum is "
                          "exact, so the fp16 outputs must equal the oracle's bit for bit",
-            "integer_work": "pack / unpack / quantise codes: bit-exact",
+            "integer_work": "pack / unpack / quantise codes, MoE routing offsets: bit-exact",
+            "unordered": "rows inside one expert after routing: any order; checked as a valid permutation",
         },
     }
 
