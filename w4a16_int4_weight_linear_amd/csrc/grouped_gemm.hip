@@ -119,11 +119,6 @@ __device__ inline bool find_item(const int32_t* __restrict__ offsets, int expert
   return false;
 }
 
-// f16x2 {s, s} for half `idx` (0..3) of the dword pair (lo, hi).
-__device__ inline f16x2 pick_scale(uint32_t lo, uint32_t hi, uint32_t sel) {
-  return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, sel));
-}
-
 // One item of MB 16-row blocks (rows <= 16 * MB).  G is the group size; ALIGNED:
 // each scale row starts on a 16-byte (G = 32) or 4-byte (G = 128) boundary, so
 // one vector load brings a K step's scales.
@@ -190,9 +185,14 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
     colok[b] = n < N;
     sbase[b] = (uint32_t)n * spr * 2u;
   }
-  // G = 32, aligned: groups 8 s .. 8 s + 7 of the step
-  auto load_s32 = [&](int s, int b) -> u32x4 {
-    const uint32_t off = (colok[b] && 8 * s < (int)spr) ? sbase[b] + 16u * (uint32_t)s : kOutOfRange;
+  // G = 32, aligned, four steps per load: lane lq of row li loads the 16 bytes
+  // (8 groups) of step 4 S + lq, so one instruction reads 64 contiguous bytes of
+  // each scale row (loading each step's 16 bytes separately made the memory
+  // system fetch every scale line several times).  A lane takes its scale from
+  // the lane that loaded its step (a cross-lane read).
+  auto load_s32x4 = [&](int S, int b) -> u32x4 {
+    const int st = 4 * S + lq;
+    const uint32_t off = (colok[b] && 8 * st < (int)spr) ? sbase[b] + 16u * (uint32_t)st : kOutOfRange;
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0));
   };
   // G = 128, aligned: groups 2 s, 2 s + 1
@@ -232,7 +232,6 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
 
   // ---- prologue: kDepth steps of weights and scales, first activation block ----
   u32x4 raw[kDepth][kNB][2];
-  u32x4 s32[kDepth][kNB];
   uint32_t s128[kDepth][kNB];
   uint32_t s16[kDepth][kNB][2];
   auto issue_step = [&](int s, int slot) {
@@ -240,13 +239,20 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
     for (int b = 0; b < kNB; ++b) {
       raw[slot][b][0] = load_raw(s, b, 0);
       raw[slot][b][1] = load_raw(s, b, 1);
-      if constexpr (ALIGNED && G == 32) s32[slot][b] = load_s32(s, b);
       if constexpr (ALIGNED && G == 128) s128[slot][b] = load_s128(s, b);
       if constexpr (!ALIGNED) { s16[slot][b][0] = load_s16(s, 0, b); s16[slot][b][1] = load_s16(s, 1, b); }
     }
   };
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue_step(d, d);
+  u32x4 sq_cur[kNB], sq_nxt[kNB];                   // G = 32 aligned: scales of steps 4 S .. 4 S + 3, 4 S + 4 ..
+  if constexpr (ALIGNED && G == 32) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      sq_cur[b] = load_s32x4(0, b);
+      sq_nxt[b] = load_s32x4(1, b);
+    }
+  }
   u32x4 xv[kXPieces];
   load_x(0, xv);
   store_x(0, xv);
@@ -259,8 +265,6 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
 #pragma unroll
     for (int b = 0; b < kNB; ++b) acc[i][b] = f32x4{};
 
-  // per-lane selector of half lq of a dword pair, broadcast to both halves
-  const uint32_t sel_lq = (uint32_t)(2 * lq) * 0x00010001u + (uint32_t)(2 * lq + 1) * 0x01000100u;
   // B-operand rows: this lane reads row li (+16 i), k 32 lq + 8 w of chunk h
   const uint8_t* xfrag = lds + li * kAPitch + 64 * lq;
 
@@ -274,6 +278,18 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
     }
     u32x4 wq[2][kNB];
     f16x2 sv[2][kNB];
+    if constexpr (ALIGNED && G == 32) {
+      if ((s & 3) == 0 && s > 0) {
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+          sq_cur[b] = sq_nxt[b];
+          sq_nxt[b] = load_s32x4((s >> 2) + 1, b);
+        }
+      }
+    }
+    // lane (li, lq) needs group 8 s + 4 h + lq: dword 2 h + lq / 2, half lq & 1 of
+    // the 16 bytes that lane (li, s & 3) loaded
+    const int src_lane = 16 * (s & 3) + li;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       wq[0][b] = *reinterpret_cast<const u32x4*>(tile_r0 + b * 2048);
@@ -284,8 +300,11 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
           const _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)s16[slot][b][h]);
           sv[h][b] = f16x2{v, v};
         } else if constexpr (G == 32) {
-          const u32x4 v = s32[slot][b];
-          sv[h][b] = h ? pick_scale(v.z, v.w, sel_lq) : pick_scale(v.x, v.y, sel_lq);
+          const u32x4 v = sq_cur[b];
+          const int lo = __shfl((int)(h ? v.z : v.x), src_lane);
+          const int hi = __shfl((int)(h ? v.w : v.y), src_lane);
+          const uint32_t d = (uint32_t)((lq >> 1) ? hi : lo);
+          sv[h][b] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(d, d, (lq & 1) ? 0x03020302u : 0x01000100u));
         } else {
           const uint32_t v = s128[slot][b];
           sv[h][b] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(v, v, h ? 0x03020302u : 0x01000100u));
