@@ -142,8 +142,10 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
  * hold 2n interleaved weight rows: row 2i is the gate row of output i, row
  * 2i + 1 its up row.  y [m, n] = fp16(SiLU(g) * u) with g, u the fp32-accumulated
  * products x . row^T and SiLU(g) = g / (1 + e^-g) in fp32; the 2 x m x n
- * intermediate never leaves the chip.  Errors as w4a16_gemv (m > 16 is
- * W4A16_ERR_SHAPE); k == 0 writes zeros.
+ * intermediate never leaves the chip.  m <= 4 runs on the decode GEMV kernel
+ * (each workgroup owns whole gate/up row pairs; no workspace), larger m on the
+ * weight-streaming kernel.  Errors as w4a16_gemv (m > 16 is W4A16_ERR_SHAPE);
+ * k == 0 writes zeros.
  */
 int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                       uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group, void* stream);

@@ -37,8 +37,12 @@ def run(w4, x, p, s, group):
 
 
 # (m, n outputs, k, group): ragged n, a K tail inside a line, odd scale counts,
-# partial activation chunks, both group sizes, 1 / 4 / 9 / 16 rows.
-CASES = [(1, 300, 2080, 32), (4, 1000, 5120, 128), (16, 17, 384, 128), (9, 2049, 6144, 32), (16, 512, 2048, 128)]
+# partial activation chunks, both group sizes, 1 to 4 rows (the decode GEMV with
+# the gate/up epilogue: odd pair counts, fewer pairs than CUs, a K long enough to
+# need more workgroups than CUs) and 9 / 16 rows (the weight-streaming kernel).
+CASES = [(1, 300, 2080, 32), (2, 777, 1536, 128), (3, 129, 640, 32), (4, 1000, 5120, 128), (1, 17, 384, 128),
+         (4, 301, 16384, 128), (2, 5, 8192, 32),
+         (16, 17, 384, 128), (9, 2049, 6144, 32), (16, 512, 2048, 128)]
 
 
 @pytest.mark.parametrize("m,n,k,group", CASES)
@@ -58,6 +62,32 @@ def test_swiglu_27b_gate_up_full_size(w4):
     y = run(w4, x, p, s, 128)
     rep = assert_close(y, oracle.swiglu_linear(x, p_ref, s_ref, 128), "27B gate/up")
     print(f"27B gate/up M=4: {rep.message}")
+
+
+def test_swiglu_27b_gate_up_decode_full_size(w4):
+    """The same gate/up pair at M = 1 (one decode token), every output checked."""
+    rng = np.random.default_rng(8150)
+    (p, s), (p_ref, s_ref) = gate_up_sides(w4, rng, 17408, 5120, 128)
+    x = synth.activations(rng, 1, 5120)
+    y = run(w4, x, p, s, 128)
+    rep = assert_close(y, oracle.swiglu_linear(x, p_ref, s_ref, 128), "27B gate/up M=1")
+    print(f"27B gate/up M=1: {rep.message}")
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_swiglu_exact_zeros_decode(w4, m):
+    """Integer codes and power-of-two scales on the decode path: zero ups give exact zeros, repeated calls agree bit for bit."""
+    rng = np.random.default_rng(8250 + m)
+    n, k = 333, 2048
+    q = synth.integer_codes(rng, 2 * n, k)
+    s = synth.power_of_two_scales(rng, 2 * n, k // 32, lo=-6, hi=-3)
+    x = synth.activations(rng, m, k)
+    p = w4.pack(q)
+    s_up0 = s.copy(); s_up0[1::2] = 0
+    assert np.all(run(w4, x, p, s_up0, 32).astype(np.float64) == 0)
+    y1, y2 = run(w4, x, p, s, 32), run(w4, x, p, s, 32)
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    assert_close(y1, oracle.swiglu_linear(x, oracle.pack(q), s, 32), f"integer family m={m}")
 
 
 def test_swiglu_exact_zeros_and_determinism(w4):

@@ -202,6 +202,18 @@ int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t*
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));   // SiLU(0) * 0
+  // Up to four rows: the decode GEMV kernels with the gate/up epilogue (three or
+  // four rows on MFMA, as for the plain product), while the activations fit in LDS.
+  int mb = 0;
+  size_t mlds = 0;
+  if (m >= 3 && m <= 4 && w4a16::gemv_mfma_plan((int)m, (int)(2 * n), (int)k, dev, &mb, &mlds, true))
+    return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)(2 * n), (int)k, group, mb, mlds,
+                                             dev, st, true));
+  if (m <= 4) {
+    const w4a16::GemvPlan plan = w4a16::gemv_plan((int)m, (int)(2 * n), (int)k, group, dev, true);
+    if (plan.ok)
+      return status_of(w4a16::launch_gemv(x, packed, scales, y, (int)m, (int)(2 * n), (int)k, group, plan, dev, st));
+  }
   if (!w4a16::gemm_skinny_fits(5, (int)(2 * n), (int)k, dev)) return W4A16_ERR_SHAPE;
   return status_of(w4a16::launch_swiglu_skinny(x, packed, scales, y, (int)m, (int)n, (int)k, group, dev, st));
 }

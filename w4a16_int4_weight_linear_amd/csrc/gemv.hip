@@ -47,6 +47,11 @@
 //   combined with DPP row operations plus four lane reads, and the fp32 result
 //   is rounded once to fp16.
 //
+// * Gated variant (the SwiGLU gate/up pair of an FFN): the weight rows
+//   interleave gate and up rows, workgroups own whole row pairs, and after the
+//   rows are finished one workgroup barrier lets every pair be read back from
+//   LDS and written as SiLU(gate) * up, rounded once to fp16.
+//
 // For integer x, codes and power-of-two scales every step above is exact, so
 // such inputs give bit-exact results regardless of summation order.
 #include <atomic>
@@ -108,11 +113,13 @@ constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 //   part[wave][2][4] : partial sums of the first / last row of each wave;
 //   cnt[row] : how many waves have left a partial sum of the row;
 //   res[row][m] : finished fp32 sums, written to y by the wave that finished them.
-template <int M>
+template <int M, bool GATED>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
             const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
             int n, int k, int gshift, int rows_base, int rows_extra) {
+  // rows_base / rows_extra count row units: single rows, or gate/up row pairs.
+  constexpr int kUnit = GATED ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int XS = XSumSlots<M>::value;
   constexpr int U = kLoadsInFlight;              // items in flight
@@ -127,8 +134,8 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   // wave index, made explicitly wave-uniform so the bookkeeping lives in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int blk = blockIdx.x;
-  const int nr = rows_base + (blk < rows_extra ? 1 : 0);                 // rows of this workgroup
-  const int wg_r0 = blk * rows_base + (blk < rows_extra ? blk : rows_extra);
+  const int nr = kUnit * (rows_base + (blk < rows_extra ? 1 : 0));       // rows of this workgroup
+  const int wg_r0 = kUnit * (blk * rows_base + (blk < rows_extra ? blk : rows_extra));
   const int chunks = nr * C;                                             // chunks of the block
   const int items = (chunks + 63) >> 6;                                  // 1 KiB items
   // Waves 0..W/2-1 are the older wave of their SIMD and are issued first, so
@@ -140,7 +147,7 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     return (int)((cum * (uint32_t)items) / (uint32_t)(kGemvWaves * 1024));
   };
   const int t0 = bound(wave), t1 = bound(wave + 1);                      // this wave's items
-  const GemvLayout L = gemv_layout(M, C, spr, rows_base + (rows_extra ? 1 : 0));
+  const GemvLayout L = gemv_layout(M, C, spr, kUnit * (rows_base + (rows_extra ? 1 : 0)));
 
   // ---- staging loads (activations, scales), issued before the weight stream ----
   const uint32_t sc_begin = (uint32_t)wg_r0 * (uint32_t)spr * 2u;
@@ -477,6 +484,18 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     if (last_cut) comb_last = count_in(r_last_w);
   }
 
+  if constexpr (GATED) {
+    // Every row of the workgroup is in res once all waves have passed this point.
+    __syncthreads();
+    const int pairs_wg = nr >> 1, n_out = n >> 1;
+    for (int e = threadIdx.x; e < pairs_wg * M; e += kGemvThreads) {
+      const int pr = e / M, m = e - (e / M) * M;
+      const float g = res[(2 * pr) * M + m], u = res[(2 * pr + 1) * M + m];
+      y[(size_t)m * n_out + (wg_r0 >> 1) + pr] = float_to_half_bits(g / (1.f + __expf(-g)) * u);
+    }
+    return;
+  }
+
   // ---- y for the rows this wave finished: whole rows, and cut rows it combined ----
   if (cnt_items > 0) {
     const int c_lo = t0 << 6, c_hi = min(t1 << 6, chunks);
@@ -495,45 +514,50 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   }
 }
 
-template <int M>
+template <int M, bool GATED>
 hipError_t launch_gemv_m(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
                          int n, int k, int group, const GemvPlan& plan, const DeviceInfo& dev,
                          hipStream_t stream) {
   static std::atomic<uint64_t> attr_set{0};   // one bit per device
   const uint64_t bit = 1ull << (dev.device & 63);
   if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<M>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<M, GATED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   const int gshift = group == 128 ? 2 : 0;   // log2(group / 32)
   (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL(gemv_kernel<M>, dim3(plan.blocks), dim3(kGemvThreads), plan.lds, stream, x, packed, scales, y,
+  hipLaunchKernelGGL((gemv_kernel<M, GATED>), dim3(plan.blocks), dim3(kGemvThreads), plan.lds, stream, x, packed, scales, y,
                      n, k, gshift, plan.rows_base, plan.rows_extra);
   return hipGetLastError();
 }
 
-size_t plan_lds(int m, int n, int k, int group, int blocks) {
+size_t plan_lds(int m, int units, int k, int group, int blocks, int unit) {
   const int C = k / 32;
   const int spr = C / (group / 32);
-  const int rows_base = n / blocks, rows_extra = n % blocks;
-  return gemv_layout(m, C, spr, rows_base + (rows_extra ? 1 : 0)).total;
+  const int base = units / blocks, extra = units % blocks;
+  return gemv_layout(m, C, spr, unit * (base + (extra ? 1 : 0))).total;
 }
 
 }  // namespace
 
-GemvPlan gemv_plan(int m, int n, int k, int group, const DeviceInfo& dev) {
+GemvPlan gemv_plan(int m, int n, int k, int group, const DeviceInfo& dev, bool gated) {
   GemvPlan p;
+  // Rows are handed out in units: single rows, or gate/up row pairs (n even).
+  const int unit = gated ? 2 : 1;
+  const int units = n / unit;
+  p.gated = gated;
+  if (units <= 0 || units * unit != n) return p;
   // One workgroup per CU; more (fewer rows, so fewer staged scales, each) until the LDS fits.
-  int blocks = n < dev.num_cu ? n : dev.num_cu;
-  while (blocks < n && plan_lds(m, n, k, group, blocks) > dev.max_lds) {
-    blocks = blocks * 2 < n ? blocks * 2 : n;
+  int blocks = units < dev.num_cu ? units : dev.num_cu;
+  while (blocks < units && plan_lds(m, units, k, group, blocks, unit) > dev.max_lds) {
+    blocks = blocks * 2 < units ? blocks * 2 : units;
   }
   p.blocks = blocks;
-  p.rows_base = n / blocks;
-  p.rows_extra = n % blocks;
-  p.lds = plan_lds(m, n, k, group, blocks);
+  p.rows_base = units / blocks;
+  p.rows_extra = units % blocks;
+  p.lds = plan_lds(m, units, k, group, blocks, unit);
   p.ok = p.lds <= dev.max_lds;
   return p;
 }
@@ -551,11 +575,20 @@ int64_t gemv_max_k(int m, int group, const DeviceInfo& dev) {
 
 hipError_t launch_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                        int n, int k, int group, const GemvPlan& plan, const DeviceInfo& dev, hipStream_t stream) {
+  if (plan.gated) {
+    switch (m) {
+      case 1: return launch_gemv_m<1, true>(x, packed, scales, y, n, k, group, plan, dev, stream);
+      case 2: return launch_gemv_m<2, true>(x, packed, scales, y, n, k, group, plan, dev, stream);
+      case 3: return launch_gemv_m<3, true>(x, packed, scales, y, n, k, group, plan, dev, stream);
+      case 4: return launch_gemv_m<4, true>(x, packed, scales, y, n, k, group, plan, dev, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (m) {
-    case 1: return launch_gemv_m<1>(x, packed, scales, y, n, k, group, plan, dev, stream);
-    case 2: return launch_gemv_m<2>(x, packed, scales, y, n, k, group, plan, dev, stream);
-    case 3: return launch_gemv_m<3>(x, packed, scales, y, n, k, group, plan, dev, stream);
-    case 4: return launch_gemv_m<4>(x, packed, scales, y, n, k, group, plan, dev, stream);
+    case 1: return launch_gemv_m<1, false>(x, packed, scales, y, n, k, group, plan, dev, stream);
+    case 2: return launch_gemv_m<2, false>(x, packed, scales, y, n, k, group, plan, dev, stream);
+    case 3: return launch_gemv_m<3, false>(x, packed, scales, y, n, k, group, plan, dev, stream);
+    case 4: return launch_gemv_m<4, false>(x, packed, scales, y, n, k, group, plan, dev, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -59,11 +59,15 @@ __host__ inline size_t lds_bytes(int m, int k, int blocks) {
   return main > red ? main : red;
 }
 
-template <int M, int G, bool ALIGNED>
+// GATED: the N weight rows interleave the gate and up rows of a SwiGLU pair;
+// workgroups own whole pairs (rows_base / rows_extra count pairs) and
+// y[m, N / 2] = SiLU(gate) * up.
+template <int M, int G, bool ALIGNED, bool GATED>
 __global__ void __launch_bounds__(kThreads)
 gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                  const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
                  int N, int K, int rows_base, int rows_extra) {
+  constexpr int kUnit = GATED ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -72,8 +76,8 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   const int li = lane & 15;
 
   const int blk = blockIdx.x;
-  const int nr = rows_base + (blk < rows_extra ? 1 : 0);
-  const int r0 = blk * rows_base + (blk < rows_extra ? blk : rows_extra);
+  const int nr = kUnit * (rows_base + (blk < rows_extra ? 1 : 0));
+  const int r0 = kUnit * (blk * rows_base + (blk < rows_extra ? blk : rows_extra));
   const int nb = (nr + 15) >> 4;                  // 16-row blocks (<= kMaxBlocks, checked on the host)
   const int lines = (K + KL - 1) / KL;
   const int units = nb * lines;
@@ -230,20 +234,30 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
     f32x4 t = red[wave * 64 + lane];
     for (int w = 1; w < kWaves; ++w) t += red[(w * kMaxBlocks + wave) * 64 + lane];
     // lane holds weight rows 4 lq .. 4 lq + 3 of block `wave` for activation row li
+    if constexpr (GATED) {
+      // r0 and nr are even, so rows 4 lq + j, 4 lq + j + 1 are one (gate, up) pair
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = 16 * wave + 4 * lq + j;
-      if (rr < nr) y[(size_t)li * N + r0 + rr] = float_to_half_bits(t[j]);
+      for (int j = 0; j < 4; j += 2) {
+        const int rr = 16 * wave + 4 * lq + j;
+        const float g = t[j];
+        if (rr < nr) y[(size_t)li * (N >> 1) + ((r0 + rr) >> 1)] = float_to_half_bits(g / (1.f + __expf(-g)) * t[j + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 16 * wave + 4 * lq + j;
+        if (rr < nr) y[(size_t)li * N + r0 + rr] = float_to_half_bits(t[j]);
+      }
     }
   }
 }
 
-template <int M, int G, bool ALIGNED>
+template <int M, int G, bool ALIGNED, bool GATED>
 hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
                     int blocks, size_t lds, const DeviceInfo& dev, hipStream_t stream) {
   static std::atomic<uint64_t> attr_set{0};   // one bit per device
   const uint64_t bit = 1ull << (dev.device & 63);
-  auto kern = gemv_mfma_kernel<M, G, ALIGNED>;
+  auto kern = gemv_mfma_kernel<M, G, ALIGNED, GATED>;
   if (!(attr_set.load(std::memory_order_acquire) & bit)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
@@ -251,32 +265,38 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* s
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, x, packed, scales, y, n, k, n / blocks,
-                     n % blocks);
+  const int units = GATED ? n / 2 : n;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, x, packed, scales, y, n, k, units / blocks,
+                     units % blocks);
   return hipGetLastError();
 }
 
-template <int M>
+template <int M, bool GATED>
 hipError_t launch_g(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
                     int group, int blocks, size_t lds, const DeviceInfo& dev, hipStream_t stream) {
   const int spr = k / group;
   if (group == 32)
-    return spr % 8 == 0 ? launch_m<M, 32, true>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
-                        : launch_m<M, 32, false>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
-  return spr % 2 == 0 ? launch_m<M, 128, true>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
-                      : launch_m<M, 128, false>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
+    return spr % 8 == 0 ? launch_m<M, 32, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
+                        : launch_m<M, 32, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
+  return spr % 2 == 0 ? launch_m<M, 128, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
+                      : launch_m<M, 128, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
 }
 
 }  // namespace
 
-bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, size_t* lds) {
+bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, size_t* lds, bool gated) {
   if (m < 2 || m > 4 || n <= 0 || k <= 0) return false;
+  // Rows are handed out in units: single rows, or (gate, up) row pairs.
+  const int unit = gated ? 2 : 1;
+  if (n % unit) return false;
+  const int units = n / unit;
   // Two workgroups per CU, more if a workgroup would exceed kMaxBlocks row blocks.
   int g = W4A16_GEMVM_WG_PER_CU * dev.num_cu;
   if ((int64_t)g * 16 > n) g = (n + 15) / 16;
-  const int per = 16 * kMaxBlocks;
-  if ((int64_t)g * per < n) g = (n + per - 1) / per;
-  const int rows_max = n / g + (n % g ? 1 : 0);
+  const int per = 16 * kMaxBlocks / unit;
+  if ((int64_t)g * per < units) g = (units + per - 1) / per;
+  if (g > units) g = units;
+  const int rows_max = unit * (units / g + (units % g ? 1 : 0));
   const size_t bytes = lds_bytes(m, k, (rows_max + 15) / 16);
   if (bytes > dev.max_lds) return false;
   *blocks = g;
@@ -286,11 +306,19 @@ bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, siz
 
 hipError_t launch_gemv_mfma(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                             int n, int k, int group, int blocks, size_t lds, const DeviceInfo& dev,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool gated) {
+  if (gated) {
+    switch (m) {
+      case 2: return launch_g<2, true>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
+      case 3: return launch_g<3, true>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
+      case 4: return launch_g<4, true>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (m) {
-    case 2: return launch_g<2>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
-    case 3: return launch_g<3>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
-    case 4: return launch_g<4>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
+    case 2: return launch_g<2, false>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
+    case 3: return launch_g<3, false>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
+    case 4: return launch_g<4, false>(x, packed, scales, y, n, k, group, blocks, lds, dev, stream);
     default: return hipErrorInvalidValue;
   }
 }

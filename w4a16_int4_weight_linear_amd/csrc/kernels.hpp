@@ -21,12 +21,14 @@ hipError_t current_device_info(DeviceInfo* out);
 
 // ---- decode GEMV (gemv.hip) ----
 struct GemvPlan {
-  int blocks = 0, rows_base = 0, rows_extra = 0;   // workgroups; rows per workgroup (+1 for the first rows_extra)
-  size_t lds = 0;     // bytes of LDS per workgroup
-  bool ok = false;    // false: the activations and scales do not fit in LDS
+  int blocks = 0, rows_base = 0, rows_extra = 0;   // workgroups; row units per workgroup (+1 for the first rows_extra)
+  size_t lds = 0;       // bytes of LDS per workgroup
+  bool ok = false;      // false: the activations and scales do not fit in LDS
+  bool gated = false;   // SwiGLU pairs: row units are (gate, up) row pairs, y gets n / 2 columns
 };
-// Launch plan (work split and LDS size) for an m x k by n x k problem.
-GemvPlan gemv_plan(int m, int n, int k, int group, const DeviceInfo& dev);
+// Launch plan (work split and LDS size) for an m x k by n x k problem; gated:
+// the n weight rows interleave gate and up rows and y[m, n / 2] = SiLU(gate) * up.
+GemvPlan gemv_plan(int m, int n, int k, int group, const DeviceInfo& dev, bool gated = false);
 // Largest k (a multiple of group) that has a feasible plan for every n.
 int64_t gemv_max_k(int m, int group, const DeviceInfo& dev);
 hipError_t launch_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
@@ -35,10 +37,11 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t
 
 // ---- batched decode GEMV on MFMA, 2 <= m <= 4 (gemv_mfma.hip) ----
 // Workgroup count and LDS bytes; false if the activations do not fit in LDS.
-bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, size_t* lds);
+// gated: the n weight rows interleave SwiGLU gate and up rows and y[m, n / 2] = SiLU(gate) * up.
+bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, size_t* lds, bool gated = false);
 hipError_t launch_gemv_mfma(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                             int n, int k, int group, int blocks, size_t lds, const DeviceInfo& dev,
-                            hipStream_t stream);
+                            hipStream_t stream, bool gated = false);
 
 // ---- 5 <= m <= 16 rows, weight-streaming on MFMA (gemm_skinny.hip) ----
 bool gemm_skinny_fits(int m, int n, int k, const DeviceInfo& dev);
