@@ -226,7 +226,7 @@ def decode_component(torch, w4, synth, args):
         "ms_per_step": ms,
         "step_bytes": step_bytes,
         "gbs": step_bytes / (ms * 1e-3) / 1e9,
-        "kernel": {"name": "gemv_kernel<1>", "launch_ms_up": up_mean, "launch_ms_down": dn_mean,
+        "kernel": {"name": "gemv_kernel<1, false>", "launch_ms_up": up_mean, "launch_ms_down": dn_mean,
                    "launch_ms_median_up": up_med, "launch_ms_median_down": dn_med,
                    "launch_ms": launch_ms, "bytes_per_launch": launch_bytes,
                    "gbs": launch_bytes / (launch_ms * 1e-3) / 1e9},
@@ -446,7 +446,7 @@ def traffic_reduce(fetch_csv, write_csv):
                 v = float(r["Counter_Value"]) * 1024.0
                 if "neg_kernel" in r["Kernel_Name"]:
                     copies.append(v)
-                elif "gemv_kernel<1>" in r["Kernel_Name"]:
+                elif "gemv_kernel<1, false>" in r["Kernel_Name"]:
                     gemv.append(v)
         if not copies or not gemv:
             raise SystemExit(f"{path}: copy or gemv dispatches missing")
@@ -458,7 +458,7 @@ def traffic_reduce(fetch_csv, write_csv):
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
     per_launch = [f * f_scale + w * w_scale for f, w in zip(f_gemv, w_gemv)]
     rec = {
-        "kernel": "gemv_kernel<1>",
+        "kernel": "gemv_kernel<1, false>",
         "workload": "decode GEMV M=1, up K=5120->N=17408 and down K=17408->N=5120, g128",
         "source_hash": source_hash("gemv.hip", "device.hpp"),
         "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
@@ -482,15 +482,18 @@ def trace_summary(trace_csv, command):
     import statistics
     from collections import defaultdict
     labels = {"gemm_kernel": ["M=512", "M=4096"],
-              "gemv_kernel<1>": ["one of up 5120->17408 / down 17408->5120 (same bytes)"],
-              "gemv_mfma_kernel<4": ["N=5120", "N=17408"],
-              "gemm_skinny_kernel<128, true, true>": ["M=1, gate+up 5120->2x17408 (SwiGLU)",
-                                                      "M=4, gate+up 5120->2x17408 (SwiGLU)"],
+              "gemv_kernel<1, false>": ["one of up 5120->17408 / down 17408->5120 (same bytes)"],
+              "gemv_kernel<1, true>": ["M=1, gate+up 5120->2x17408 (SwiGLU)"],
+              "gemv_mfma_kernel<4, 128, true, false>": ["N=5120", "N=17408"],
+              "gemv_mfma_kernel<4, 128, true, true>": ["M=4, gate+up 5120->2x17408 (SwiGLU)"],
               "gemm_skinny_kernel": ["M=16, up 5120->17408 (batched decode)"],
               "grouped_gemm_kernel": ["256 experts x [512 x 2048] g32, 4096 routed rows, uniform top-8",
-                                      "same bank, Zipf-skewed top-8 (244 experts used)"]}
-    files = {"gemv_kernel<1>": "gemv_m1_decode_27b_ffn", "gemv_mfma_kernel<4": "gemv_m4_np4_27b_ffn",
-             "gemm_skinny_kernel<128, true, true>": "swiglu_gate_up_27b",
+                                      "same bank, Zipf-skewed top-8 (244 experts used)",
+                                      "uniform routing, rows gathered by token index (inside the whole MoE layer)",
+                                      "uniform routing, rows gathered by token index (product alone)"]}
+    files = {"gemv_kernel<1, false>": "gemv_m1_decode_27b_ffn", "gemv_kernel<1, true>": "swiglu_gate_up_27b",
+             "gemv_mfma_kernel<4, 128, true, false>": "gemv_m4_np4_27b_ffn",
+             "gemv_mfma_kernel<4, 128, true, true>": "swiglu_gate_up_27b",
              "gemm_skinny_kernel": "gemm_skinny_m16_27b_up",
              "gemm_kernel": "gemm_prefill_27b_ffn", "grouped_gemm_kernel": "grouped_gemm_moe_256e"}
     groups = defaultdict(list)
@@ -540,10 +543,15 @@ def trace_summary(trace_csv, command):
             for name, c in named:
                 out[base].append((k, name, grid, wg, lds, vgpr, agpr, len(c), statistics.mean(c),
                                   statistics.median(c), min(c), max(c)))
+    # One file per workload family (the SwiGLU pair runs on two kernels).
+    by_file = defaultdict(list)
     for base, lst in out.items():
-        path = os.path.join(ROOT, "profiles", f"{files[base]}.kernel_trace.md")
+        by_file[files[base]].append((base, lst))
+    for fname, parts in by_file.items():
+        lst = [row for _, part in parts for row in part]
+        path = os.path.join(ROOT, "profiles", f"{fname}.kernel_trace.md")
         with open(path, "w") as f:
-            f.write(f"# {base}: rocprofv3 kernel trace of bench.py\n\n")
+            f.write(f"# {' and '.join(b for b, _ in parts)}: rocprofv3 kernel trace of bench.py\n\n")
             f.write("Command (from the repository root on the GPU box), then the summary:\n\n```\n"
                     f"{command}\npython3 bench.py --trace-summary <trace dir>/bench_kernel_trace.csv '<command>'\n```\n\n")
             f.write("Launches of one kernel with the same grid are split into workloads (run one after "
