@@ -39,9 +39,10 @@ def run(w4, x, p, s, group):
 # (m, n outputs, k, group): ragged n, a K tail inside a line, odd scale counts,
 # partial activation chunks, both group sizes, 1 to 4 rows (the decode GEMV with
 # the gate/up epilogue: odd pair counts, fewer pairs than CUs, a K long enough to
-# need more workgroups than CUs) and 9 / 16 rows (the weight-streaming kernel).
+# need more workgroups than CUs, and one too long for their LDS staging, which
+# falls back to the weight-streaming kernel) and 9 / 16 rows (that kernel).
 CASES = [(1, 300, 2080, 32), (2, 777, 1536, 128), (3, 129, 640, 32), (4, 1000, 5120, 128), (1, 17, 384, 128),
-         (4, 301, 16384, 128), (2, 5, 8192, 32),
+         (4, 301, 16384, 128), (2, 5, 8192, 32), (1, 64, 65536, 128),
          (16, 17, 384, 128), (9, 2049, 6144, 32), (16, 512, 2048, 128)]
 
 
