@@ -120,11 +120,16 @@ def timed(torch, fn, steps, warmup, graph=False, outputs=()):
     """Mean ms per call of fn(i) over `steps` calls, HIP events on the current stream.
 
     graph=True: the calls are captured once in a HIP graph and replayed, so the
-    host's per-call launch cost (Python + ctypes) does not enter the timing."""
+    host's per-call launch cost (Python + ctypes) does not enter the timing.  The
+    graph is replayed once untimed first (a graph's first replay carries one-off
+    setup, measured at 2-3% of a decode step), then exactly once timed."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     g = _graph_of(torch, fn, steps) if graph else None
+    if g is not None:
+        g.replay()
+        torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     if g is not None:
