@@ -5,10 +5,10 @@
 // pp1024, pp4096 columns).  Here the layer is a dense contraction, so it runs
 // on the matrix cores: v_mfma_f32_32x32x16_f16, fp16 inputs, fp32 accumulation.
 //
-// * Tiles: 128 x 256 outputs, K steps of 128.  One persistent 256-thread
-//   workgroup per CU; each of its four wavefronts (one per SIMD) owns a
-//   128 x 64 slab (4 x 2 MFMA blocks of 32 x 32, 128 fp32 accumulators per
-//   lane, kept in the accumulation registers).
+// * Tiles: 128 x 256 outputs, K steps of 128.  One persistent 512-thread
+//   workgroup per CU; each of its eight wavefronts (two per SIMD, so one can
+//   issue while the other waits on LDS or its dequantisation) owns a 128 x 32
+//   slab (4 MFMA blocks of 32 x 32, 64 fp32 accumulators per lane).
 // * The activation tile (128 x 128 fp16) and the packed weight tile (256 rows
 //   x 64 bytes) of a K step go through a three-stage LDS ring (144 KB): they
 //   are loaded straight from global memory into LDS (buffer loads with the
@@ -50,11 +50,12 @@
 namespace w4a16 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWGPerCU = 1;
 constexpr int BM = 128, BN = 256, BK = 128;
-constexpr int kWaveN = 64;                  // output columns per wave
+constexpr int kWaveN = 32;                  // output columns per wave
 constexpr int kMB = BM / 32, kNB = kWaveN / 32;
+constexpr int kWaves = kThreads / 64;
 constexpr int kSub = BK / 16;               // MFMA sub-steps per K step
 constexpr int kABytes = BM * BK * 2;        // activation tile: 128 rows of 256 bytes
 constexpr int kBBytes = BN * BK / 2;        // packed weight tile: 256 rows of 64 bytes
@@ -137,10 +138,10 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Order of one MFMA sub-step's instructions: each of its 8 MFMAs is
+// Order of one MFMA sub-step's instructions: each of its 4 MFMAs is
 // followed by up to five VALU instructions (the dequantisation of the next
-// sub-step), the first four also by one LDS read (operands two sub-steps
-// ahead) and one global load.  A scheduling fence after every sub-step keeps
+// sub-step) and by one LDS read (operands two sub-steps ahead) and one global
+// load.  A scheduling fence after every sub-step keeps
 // the reads two sub-steps ahead of their use.
 __device__ inline void schedule_substep() {
 #pragma unroll
@@ -223,13 +224,13 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(packed, (uint32_t)N * wrow);
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, (uint32_t)N * spr * 2u);
   // fp32 partial tiles: slot p at p * kPartialBytes; inside a slot, 16-byte
-  // quad q of accumulator block blk of thread t at ((blk * 4 + q) * 256 + t) * 16,
+  // quad q of accumulator block blk of thread t at ((blk * 4 + q) * kThreads + t) * 16,
   // so every store or load instruction covers 1 KB contiguously
   const __amdgpu_buffer_rsrc_t pres = make_rsrc(partials, partials ? 2u * (uint32_t)wgs * (uint32_t)kPartialBytes : 0u);
 
   // ---- LDS layouts and per-lane offsets (the same for every tile)
   // Activations: row r of 256 bytes, 16-byte chunk c stored at c ^ (r % 16).
-  // Load j of wave w fills rows 16 j + 4 w .. + 3 (lane i: row + i / 16,
+  // Load j of wave w fills rows 32 j + 4 w .. + 3 (lane i: row + i / 16,
   // stored chunk i % 16, so it fetches chunk (i % 16) ^ (row % 16)).
   const int a_row = tid >> 4;                                   // + 16 j
   const int a_chunk = (tid & 15) ^ (a_row & 15);
@@ -237,16 +238,18 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   uint32_t a_r[kSub];
 #pragma unroll
   for (int s = 0; s < kSub; ++s) a_r[s] = (uint32_t)li * 256u + (uint32_t)(((8 * h + s) ^ (li & 15)) << 4);
+  // Scale rows are loaded 64 per wave, so the first BN / 64 waves load them.
+  const bool scale_wave = wave < BN / 64;
   // Weights: row n of 64 bytes, chunk c stored at c ^ ((n / 4) % 4).  Load j
-  // of wave w fills rows 64 j + 16 w .. + 15 (lane i: row + i / 4).
+  // of wave w fills rows 128 j + 16 w .. + 15 (lane i: row + i / 4).
   const int b_row = tid >> 2;                                   // + 64 j
   const int b_chunk = (tid & 3) ^ ((b_row >> 2) & 3);
   // Operand reads: lane (li, h) of column block nb takes k = 64 h .. + 64 of
-  // column 64 wave + 32 nb + li, as two chunks (half hf: sub-steps 4 hf ..).
+  // column kWaveN wave + 32 nb + li, as two chunks (half hf: sub-steps 4 hf ..).
   uint32_t b_r[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
-    b_r[hf] = (uint32_t)(wave * 64 + li) * 64u + (uint32_t)(((2 * h + hf) ^ ((li >> 2) & 3)) << 4);
+    b_r[hf] = (uint32_t)(wave * kWaveN + li) * 64u + (uint32_t)(((2 * h + hf) ^ ((li >> 2) & 3)) << 4);
 
   const int ktail = KTAIL ? iters - 1 : -1;
   const int krem = K - (iters - 1) * BK;                     // k in the last step
@@ -281,26 +284,24 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     return it;
   };
 
-  // Part p of step kt into LDS stage st: activations (p < 4: loads 2 p,
-  // 2 p + 1), weights (p = 4, 5: loads 2 (p - 4) ..), and without SALIGN the
-  // step's scales (p = 6).  In the last step of a K that is not a multiple of
+  // Part p of step kt into LDS stage st: activations (p < 4: load p),
+  // weights (p = 4, 5: load p - 4), and without SALIGN the step's scales
+  // (p = 6).  In the last step of a K that is not a multiple of
   // 128, chunks and groups past K are sent outside the buffer.
   auto load_part = [&](const Item& it, int kt, int st, int p) {
     const bool tail = KTAIL && kt == ktail;
     uint8_t* base = stage(st);
     if (p < 4) {
-#pragma unroll
-      for (int j = 2 * p; j < 2 * p + 2; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, W4A16_LDS(base + (16 * j + 4 * wave) * 256), 16,
-                                                 (tail && !a_tail_ok) ? kOutOfRange : a_v,
-                                                 (uint32_t)(it.m0 + 16 * j) * kbytes + (uint32_t)kt * (BK * 2), 0, 0);
+      const int j = p;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, W4A16_LDS(base + (32 * j + 4 * wave) * 256), 16,
+                                               (tail && !a_tail_ok) ? kOutOfRange : a_v,
+                                               (uint32_t)(it.m0 + 32 * j) * kbytes + (uint32_t)kt * (BK * 2), 0, 0);
     } else if (p < 6) {
-#pragma unroll
-      for (int j = 2 * (p - 4); j < 2 * (p - 4) + 2; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, W4A16_LDS(base + kABytes + (64 * j + 16 * wave) * 64), 16,
-                                                 (tail && !b_tail_ok) ? kOutOfRange : b_v,
-                                                 (uint32_t)(it.n0 + 64 * j) * wrow + (uint32_t)kt * (BK / 2), 0, 0);
-    } else if (p == 6 && !SALIGN) {
+      const int j = p - 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, W4A16_LDS(base + kABytes + (128 * j + 16 * wave) * 64), 16,
+                                               (tail && !b_tail_ok) ? kOutOfRange : b_v,
+                                               (uint32_t)(it.n0 + 128 * j) * wrow + (uint32_t)kt * (BK / 2), 0, 0);
+    } else if (p == 6 && !SALIGN && scale_wave) {
       // row n's kGroups scales at n * kGroups * 4; load q of wave v covers
       // rows 64 v + 16 q .. (g 32, lane i: row + i / 4, group i % 4) or
       // rows 64 v .. + 63 (g 128, lane i: row + i)
@@ -319,12 +320,13 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     for (int p = 0; p < 7; ++p) load_part(it, kt, st, p);
   };
   // Scale windows (SALIGN): groups [8 w, 8 w + 8) of all 256 rows of the
-  // tile, [row][8 x 2 bytes] in buffer w % 2; wave v loads rows 64 v .. + 63
-  // (lane i: row 64 v + i, 16 bytes).
+  // tile, [row][8 x 2 bytes] in buffer w % 2; wave v < 4 loads rows 64 v .. + 63
+  // (lane i: row 64 v + i, 16 bytes), the other waves' loads go to the dummy area.
   auto load_window = [&](const Item& it, int w, bool live) {
     if constexpr (SALIGN)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(live ? swin + (w & 1) * kWinBytes + 64 * wave * 16 : sdummy),
-                                               16, live ? s_v : kOutOfRange, (uint32_t)it.n0 * spr * 2u + (uint32_t)w * 16u,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, W4A16_LDS(live && scale_wave ? swin + (w & 1) * kWinBytes + 64 * wave * 16
+                                                                                   : sdummy),
+                                               16, live && scale_wave ? s_v : kOutOfRange, (uint32_t)it.n0 * spr * 2u + (uint32_t)w * 16u,
                                                0, 0);
   };
   auto window_of = [&](int kt) { return (kt * kGroups) >> 3; };
@@ -354,7 +356,7 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const int e = kt * kGroups - 8 * w + (kGroups == 1 ? 0 : 2 * h + hf);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      const int row = wave * 64 + nb * 32 + li;
+      const int row = wave * kWaveN + nb * 32 + li;
       const uint8_t* p = SALIGN ? swin + (w & 1) * kWinBytes + row * 16 + e * 2
                                 : stage(st) + kStageBytes + row * (kGroups * 4) + (kGroups == 1 ? 0 : (2 * h + hf) * 4);
       dst[nb] = *reinterpret_cast<const uint16_t*>(p);
@@ -479,13 +481,14 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     if (dp) {
       // Output through LDS (stage 2, free once the last step's barrier has
       // passed; the next item's first load into it follows that item's first
-      // barrier): each wave writes its 128 x 64 fp16 slab in two passes of 64
-      // rows into its own 9 KB, [row][64 columns] with a 144-byte row pitch
-      // (every write offset a constant, reads nearly free of bank
-      // conflicts), then stores whole 16-byte chunks, 8 lanes per 128-byte
-      // row.  The accumulator of lane (li, h) holds column li of each block,
-      // rows 8 * (r / 4) + 4 * h + r % 4.
-      constexpr int kPitch = 144;
+      // barrier): each wave writes its 128 x 32 fp16 slab in two passes of 64
+      // rows into its own 5 KB, [row][32 columns] with an 80-byte row pitch
+      // (every write offset a constant), then stores whole 16-byte chunks,
+      // 4 lanes per 64-byte row.  The accumulator of lane (li, h) holds
+      // column li of each block, rows 8 * (r / 4) + 4 * h + r % 4.
+      constexpr int kPitch = kWaveN * 2 + 16;
+      constexpr int kRowLanes = kWaveN / 8;      // lanes per output row, 16 bytes each
+      static_assert(kWaves * 64 * kPitch <= kStageBytes, "epilogue slabs exceed stage 2");
       uint8_t* ep = stage2 + wave * 64 * kPitch;
       uint8_t* ew = ep + 4 * h * kPitch + li * 2;
 #pragma unroll
@@ -500,8 +503,8 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                   float_to_half_bits(acc[2 * pass + ii][nb][r]);
         // a wave's LDS accesses complete in order: its own writes are visible
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = 8 * j + (lane >> 3), c = lane & 7;
+        for (int j = 0; j < kRowLanes; ++j) {
+          const int row = (64 / kRowLanes) * j + lane / kRowLanes, c = lane % kRowLanes;
           const u32x4 v = *reinterpret_cast<const u32x4*>(ep + row * kPitch + c * 16);
           const int m = m0 + 64 * pass + row, n = nw + 8 * c;
           if (m < M) {
