@@ -77,3 +77,55 @@ def test_graph_replay_of_decode_chain_matches_eager(w4):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}: {name} differs from eager"
         chain()                              # eager launches between replays
         torch.cuda.synchronize()
+
+
+def test_graph_replay_of_moe_layer_matches_eager(w4):
+    """Routing on the device, the gathered grouped product and the combine, captured
+    together: the routed row order inside an expert may change between runs, the
+    offsets and the combined output may not."""
+    torch = torch_mod()
+    rng = np.random.default_rng(9200)
+    tokens, experts, topk, k, n = 96, 12, 4, 512, 256
+    wm = [synth.weights(rng, n, k) for _ in range(experts)]
+    pq = [w4.quantize(a, 32) for a in wm]
+    pm, sm = dev(np.stack([a for a, _ in pq])), dev(np.stack([b for _, b in pq]))
+    ids = dev(synth.route_uniform(rng, tokens, experts, topk).choice.astype(np.int32))
+    x = dev(synth.activations(rng, tokens, k))
+    wts = dev(synth.router_weights(rng, tokens, topk))
+    offs = torch.empty(experts + 1, dtype=torch.int32, device="cuda")
+    tok = torch.empty(tokens * topk, dtype=torch.int32, device="cuda")
+    prow = torch.empty((tokens, topk), dtype=torch.int32, device="cuda")
+    yp = torch.empty((tokens * topk, n), dtype=torch.float16, device="cuda")
+    out = torch.empty((tokens, n), dtype=torch.float16, device="cuda")
+
+    def layer():
+        st = w4._stream(None)
+        rc = w4.lib.w4a16_moe_route(w4._ptr(ids), tokens, topk, experts, w4._ptr(offs), w4._ptr(tok), w4._ptr(prow), st)
+        assert rc == 0
+        w4.grouped_gemm_gather(x, tok, pm, sm, offs, 32, out=yp)
+        w4.moe_combine(yp, prow, wts, out=out)
+
+    layer()
+    torch.cuda.synchronize()
+    want_out, want_offs = out.clone(), offs.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+
+    for rep in range(4):
+        out.fill_(float("nan"))
+        offs.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(offs, want_offs), f"replay {rep}: offsets differ from eager"
+        assert torch.equal(out.view(torch.int16), want_out.view(torch.int16)), f"replay {rep}: layer output differs"
+        layer()
+        torch.cuda.synchronize()
