@@ -229,3 +229,18 @@ def test_binding_raises_on_error():
     with pytest.raises(w4.W4A16Error) as e:
         w4.quantize(np.ones((1, 48), np.float32), 32)
     assert e.value.status == w4.ERR_SHAPE
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """The package has no fallback: without libw4a16.so the import itself fails."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "w4a16_int4_weight_linear_amd")
+    pkg = tmp_path / "w4a16_int4_weight_linear_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(src, "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import w4a16_int4_weight_linear_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "is missing" in r.stderr
