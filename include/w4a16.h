@@ -22,14 +22,16 @@
  * fp16 values cross the ABI as uint16_t bit patterns.
  *
  * Conventions for every entry point:
- *   - Every return value is a w4a16_status; nothing throws, aborts or prints.
+ *   - Every entry point that can fail returns a w4a16_status; nothing throws,
+ *     aborts or prints.
  *   - Arguments are validated on the host before anything is launched; on a
  *     validation error no output is written.
  *   - m == 0, n == 0 or rows == 0 is a successful no-op.
  *   - The caller owns every buffer.  Device entry points take device pointers,
  *     run asynchronously on `stream` (a hipStream_t; NULL = the default
- *     stream) and never synchronise; host entry points take host pointers and
- *     are synchronous.
+ *     stream) and never synchronise (w4a16_gemm_workspace_status, a
+ *     diagnostic, is the one exception); host entry points take host pointers
+ *     and are synchronous.
  *   - Alignment: x, y and packed weights 16-byte aligned, scales 2-byte
  *     aligned, offsets 4-byte aligned; K must be a multiple of `group`, and
  *     `group` must be 32 or 128 (the two sizes the pages name).
@@ -46,7 +48,11 @@
 extern "C" {
 #endif
 
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
+
+/* The HIP stream type (hipStream_t is `struct ihipStream_t*`), declared here so
+ * that C callers need not include the HIP headers. */
+typedef struct ihipStream_t* w4a16_stream_t;
 
 typedef enum {
   W4A16_OK = 0,
@@ -56,8 +62,10 @@ typedef enum {
   W4A16_ERR_ALIGN = 4,     /* a pointer violates the alignment rules above */
   W4A16_ERR_WORKSPACE = 5, /* workspace missing or smaller than the query says */
   W4A16_ERR_HIP = 6,       /* the HIP runtime reported an error (launch or device query) */
-  W4A16_ERR_RANGE = 7      /* a value is out of range: a code outside [-8,7], a non-finite
+  W4A16_ERR_RANGE = 7,     /* a value is out of range: a code outside [-8,7], a non-finite
                               weight, or a group scale that overflows fp16 */
+  W4A16_ERR_TIMEOUT = 8    /* reported by w4a16_gemm_workspace_status only: a split-K fix-up of
+                              an earlier w4a16_gemm gave up waiting for a partial tile */
 } w4a16_status;
 
 /* Version of this ABI (W4A16_ABI_VERSION). */
@@ -77,17 +85,17 @@ const char* w4a16_status_str(int status);
  * Errors: NULL pointers, bad shapes/group, W4A16_ERR_RANGE for a non-finite w
  * or an s that overflows fp16 (nothing is written then).
  */
-int w4a16_quantize(const float* w, int64_t n, int64_t k, int32_t group,
-                   uint32_t* packed, uint16_t* scales);
+w4a16_status w4a16_quantize(const float* w, int64_t n, int64_t k, int32_t group,
+                            uint32_t* packed, uint16_t* scales);
 
 /*
  * Pack int8 codes q [n, k] (host, each in [-8, 7]) into uint32 [n, k/8] (host).
  * k must be a multiple of 8.  W4A16_ERR_RANGE if a code is out of range.
  */
-int w4a16_pack(const int8_t* q, int64_t n, int64_t k, uint32_t* packed);
+w4a16_status w4a16_pack(const int8_t* q, int64_t n, int64_t k, uint32_t* packed);
 
 /* Unpack uint32 [n, k/8] (host) back to int8 codes q [n, k] (host). */
-int w4a16_unpack(const uint32_t* packed, int64_t n, int64_t k, int8_t* q);
+w4a16_status w4a16_unpack(const uint32_t* packed, int64_t n, int64_t k, int8_t* q);
 
 /* -------------------------------------------------------------- device ---- */
 
@@ -95,26 +103,27 @@ int w4a16_unpack(const uint32_t* packed, int64_t n, int64_t k, int8_t* q);
  * Decode GEMV, 1 <= m <= 4 (the M = 1 decode step and the batched np4 decode
  * of the LLM170 CUDA/W4A16 page's benchmark tables): y = x . deq(W)^T.
  * All m rows share one pass over the packed weights.  x [m, k] and y [m, n]
- * fp16, packed [n, k/8], scales [n, k/group], all on the device.
- * The activations and the scales of the rows in flight are staged in on-chip
- * memory (LDS), which bounds k: every k <= w4a16_gemv_max_k(m, group) is
- * accepted; larger k may be rejected with W4A16_ERR_SHAPE (w4a16_gemm takes
- * any size).
+ * fp16, packed [n, k/8], scales [n, k/group], all on the device.  Any k (a
+ * multiple of group): up to w4a16_gemv_max_k(m, group) the activations are
+ * staged in on-chip memory (LDS) whole; longer k runs on a kernel that stages
+ * them in chunks, with the same result bars.  m > 4 is W4A16_ERR_SHAPE.
  */
-int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
-               uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
-               void* stream);
+w4a16_status w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                        uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
+                        w4a16_stream_t stream);
 
-/* Largest k w4a16_gemv accepts for every n, for m rows and this group size on
- * the current device (0 if m is outside 1..4, the group is invalid or no
- * device is usable). */
+/* Largest k for which w4a16_gemv stages the activations whole in LDS, for m
+ * rows and this group size on the current device (0 if m is outside 1..4, the
+ * group is invalid or no device is usable).  Informational: w4a16_gemv takes
+ * longer k as well. */
 int64_t w4a16_gemv_max_k(int64_t m, int32_t group);
 
 /*
  * Bytes of device workspace w4a16_gemm needs for this problem on the current
  * device (0 means none; the pointer may then be NULL).  It is 0 for the
  * weight-streaming sizes (m <= 32 where those kernels run).  Returns 0 for
- * invalid shapes as well; w4a16_gemm reports those.
+ * invalid shapes as well; w4a16_gemm reports those.  A workspace begins with a
+ * 256-byte header holding the status word of w4a16_gemm_workspace_status.
  */
 size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group);
 
@@ -129,10 +138,24 @@ size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
  * m <= 32 the product is a weight stream and runs on weight-streaming kernels
  * (m <= 4: the decode GEMV kernels), with the same result bars; those need no
  * workspace (the query returns 0) and never touch one that is passed.
+ * The split-K fix-up waits for other workgroups' partial tiles with a bounded
+ * poll (about a second).  Should it ever give up (only if the device cannot
+ * keep all of the launch's workgroups resident at once), the outputs of the
+ * affected tiles are written as fp16 NaN, the call still returns W4A16_OK, and
+ * the workspace's status word records it (w4a16_gemm_workspace_status).
  */
-int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
-               uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
-               void* workspace, size_t workspace_bytes, void* stream);
+w4a16_status w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                        uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
+                        void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
+
+/*
+ * Diagnostic, not for the hot path: waits for the work queued on `stream`,
+ * then reads the status word at the start of a w4a16_gemm workspace (device
+ * pointer, at least 256 bytes).  Returns W4A16_ERR_TIMEOUT, and clears the
+ * word, if a split-K fix-up of an earlier call on it gave up waiting (its
+ * tiles were written as NaN); else W4A16_OK.  Synchronises the host.
+ */
+w4a16_status w4a16_gemm_workspace_status(void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
 
 /*
  * Fused gate/up projection of a SwiGLU feed-forward, 1 <= m <= 16 rows (the
@@ -147,8 +170,9 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
  * weight-streaming kernel.  Errors as w4a16_gemv (m > 16 is W4A16_ERR_SHAPE);
  * k == 0 writes zeros.
  */
-int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
-                      uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group, void* stream);
+w4a16_status w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                               uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
+                               w4a16_stream_t stream);
 
 /*
  * MoE grouped GEMM (the routed-expert layers of the 35B-A3B MoE model on the
@@ -161,9 +185,10 @@ int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t*
  * x[r] . deq(W_e)^T for the expert e that owns row r.  No combine across
  * experts is done.
  */
-int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
-                       const int32_t* offsets, uint16_t* y, int32_t num_experts,
-                       int64_t rows, int64_t n, int64_t k, int32_t group, void* stream);
+w4a16_status w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                                const int32_t* offsets, uint16_t* y, int32_t num_experts,
+                                int64_t rows, int64_t n, int64_t k, int32_t group,
+                                w4a16_stream_t stream);
 
 /*
  * The routed-expert (MoE) steps either side of the grouped product, for the
@@ -179,8 +204,9 @@ int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
  * output).  An id outside [0, num_experts) gets pair_row = -1 and no row; then
  * offsets[num_experts] < tokens * topk.  1 <= num_experts <= 32768.
  */
-int w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts,
-                    int32_t* offsets, int32_t* pair_token, int32_t* pair_row, void* stream);
+w4a16_status w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts,
+                             int32_t* offsets, int32_t* pair_token, int32_t* pair_row,
+                             w4a16_stream_t stream);
 
 /*
  * w4a16_grouped_gemm with the activations gathered: x [tokens, k] holds the
@@ -188,10 +214,10 @@ int w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32
  * w4a16_moe_route), so no expert-sorted copy of x is made.  y [rows, n] as in
  * w4a16_grouped_gemm.  A pair_token outside [0, tokens) reads zeros.
  */
-int w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
-                              const uint16_t* scales, const int32_t* offsets, uint16_t* y,
-                              int32_t num_experts, int64_t rows, int64_t tokens, int64_t n, int64_t k,
-                              int32_t group, void* stream);
+w4a16_status w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
+                                       const uint16_t* scales, const int32_t* offsets, uint16_t* y,
+                                       int32_t num_experts, int64_t rows, int64_t tokens, int64_t n,
+                                       int64_t k, int32_t group, w4a16_stream_t stream);
 
 /*
  * Router-weighted combine: out [tokens, n] fp16, out[t] = sum over slots j (in
@@ -199,8 +225,9 @@ int w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, cons
  * rounded once.  y_pairs [rows, n] fp16 (the grouped product), weights fp32
  * [tokens, topk].  A pair_row outside [0, rows) contributes nothing.
  */
-int w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
-                      int64_t tokens, int32_t topk, int64_t rows, int64_t n, void* stream);
+w4a16_status w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights,
+                               uint16_t* out, int64_t tokens, int32_t topk, int64_t rows, int64_t n,
+                               w4a16_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -32,8 +32,8 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert w4.lib.w4a16_abi_version() == 1
-    for s in range(8):
+    assert w4.lib.w4a16_abi_version() == 2
+    for s in range(9):
         assert w4.lib.w4a16_status_str(s).decode().startswith("W4A16_")
     assert b"unknown" in w4.lib.w4a16_status_str(99)
 
@@ -164,6 +164,11 @@ def test_gemm_validation():
     assert g(A, A, A, A, 8, 64, 128, 128, A + 4, 0, None) == w4.ERR_ALIGN
     assert g(None, None, None, None, 0, 64, 128, 128, None, 0, None) == w4.OK
     assert w4.lib.w4a16_gemm_workspace_bytes(8, 64, 100, 32) == 0
+    st = w4.lib.w4a16_gemm_workspace_status
+    assert st(None, 4096, None) == w4.ERR_NULL
+    assert st(A + 4, 4096, None) == w4.ERR_ALIGN
+    assert st(A, 255, None) == w4.ERR_WORKSPACE     # smaller than the status header
+    assert b"TIMEOUT" in w4.lib.w4a16_status_str(w4.ERR_TIMEOUT)
 
 
 def test_gemv_swiglu_validation():

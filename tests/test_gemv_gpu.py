@@ -122,7 +122,45 @@ def test_gemv_max_k_is_usable(w4):
         s = np.full((8, k // 128), 2.0 ** -8, np.float16)
         y = run_gemv(w4, x, w4.pack(q), s, 128)
         assert_bit_exact(y, oracle.linear(x, oracle.pack(q), s, 128), f"m={m} k={k}")
-        k2 = kmax + 4096
-        with pytest.raises(w4.W4A16Error):
-            w4.gemv(dev(np.zeros((m, k2), np.float16)), dev(np.zeros((8, k2 // 8), np.uint32)),
-                    dev(np.zeros((8, k2 // 128), np.float16)), 128)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_gemv_beyond_lds_cap(w4, m):
+    """K longer than the LDS-staged decode kernels take: w4a16_gemv runs the
+    chunk-staged weight-streaming kernel instead, still bit-exact."""
+    kmax = w4.lib.w4a16_gemv_max_k(m, 128)
+    for k, group in ((kmax + 4096, 128), (kmax + 1024 + 32, 32)):
+        k = k // group * group
+        rng = np.random.default_rng(4100 + m + k)
+        x = synth.integer_activations(rng, m, k, -1, 1)
+        q = synth.integer_codes(rng, 37, k)
+        s = synth.power_of_two_scales(rng, 37, k // group, lo=-9, hi=-8)
+        y = run_gemv(w4, x, w4.pack(q), s, group)
+        assert_bit_exact(y, oracle.linear(x, oracle.pack(q), s, group), f"m={m} k={k} g={group}")
+
+
+def _offset_scales(s: np.ndarray):
+    """The scales on the device at an address 2 bytes past a 16-byte boundary."""
+    torch = torch_mod()
+    flat = torch.zeros(s.size + 8, dtype=torch.float16, device="cuda")
+    view = flat[1:1 + s.size].view(s.shape)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(s)))
+    assert view.data_ptr() % 16 == 2 and view.is_contiguous()
+    return view
+
+
+@pytest.mark.parametrize("m", [1, 3, 4, 9, 200])
+@pytest.mark.parametrize("k,group", [(2048, 32), (2304, 128), (5120, 128)])
+def test_scales_at_two_byte_offset(w4, m, k, group):
+    """Scales need only 2-byte alignment: a scale pointer 2 bytes past a 16-byte
+    boundary takes the kernels' 2-byte scale loads (or aligned staging), bit-exact."""
+    rng = np.random.default_rng(4200 + m + k + group)
+    n = 300
+    x = synth.integer_activations(rng, m, k)
+    q = synth.integer_codes(rng, n, k)
+    s = synth.power_of_two_scales(rng, n, k // group, lo=-6, hi=-3)
+    y_ref = oracle.linear(x, oracle.pack(q), s, group)
+    sd = _offset_scales(s)
+    fn = w4.gemv if m <= 4 else w4.gemm
+    y = host(fn(dev(x), dev(w4.pack(q)), sd, group))
+    assert_bit_exact(y, y_ref, f"m={m} k={k} g={group}")

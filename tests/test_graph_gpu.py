@@ -1,12 +1,14 @@
 """Decode launch chain captured in one HIP graph and replayed (the pages' CUDA-graph
 decode step): every replay must leave exactly the bits of the same launches made
-eagerly, with the program's own eager work and synchronisations between replays."""
+eagerly, with the program's own eager work and synchronisations between replays,
+and every replayed output must meet the fp64 oracle's bars."""
 
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from gpu_util import dev, torch_mod
+from gpu_util import assert_close, dev, host, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -26,15 +28,24 @@ def test_graph_replay_of_decode_chain_matches_eager(w4):
     k, n = 1024, 1536
     w = synth.weights(rng, n, k)
     p, s = w4.quantize(w, 128)
+    q_ref, s_ref = oracle.quantize(w, 128)
+    p_ref = oracle.pack(q_ref)
     pt, st = dev(p), dev(s)
-    x1 = dev(synth.activations(rng, 1, k))
-    x4 = dev(synth.activations(rng, 4, k))
-    x16 = dev(synth.activations(rng, 16, k))
+    x1n, x4n, x16n = (synth.activations(rng, m, k) for m in (1, 4, 16))
+    x1, x4, x16 = dev(x1n), dev(x4n), dev(x16n)
     wm = [synth.weights(rng, 256, 512) for _ in range(6)]
     pq = [w4.quantize(a, 32) for a in wm]
+    oq = [oracle.quantize(a, 32) for a in wm]
     pm, sm = dev(np.stack([a for a, _ in pq])), dev(np.stack([b for _, b in pq]))
     r = synth.route_uniform(rng, 40, 6, 2)
-    xm = dev(synth.activations(rng, 40, 512)[r.pair_token])
+    xmn = synth.activations(rng, 40, 512)[r.pair_token]
+    xm = dev(xmn)
+    # the oracle's outputs of the six captured products
+    refs = [oracle.linear(x1n, p_ref, s_ref, 128), oracle.linear(x4n, p_ref, s_ref, 128),
+            oracle.linear(x16n, p_ref, s_ref, 128), oracle.swiglu_linear(x1n, p_ref, s_ref, 128),
+            oracle.swiglu_linear(x4n, p_ref, s_ref, 128),
+            oracle.grouped_linear(xmn, np.stack([oracle.pack(a) for a, _ in oq]), np.stack([b for _, b in oq]),
+                                  r.offsets, 32)]
     offs = dev(r.offsets)
     y1 = torch.empty((1, n), dtype=torch.float16, device="cuda")
     y4 = torch.empty((4, n), dtype=torch.float16, device="cuda")
@@ -73,8 +84,9 @@ def test_graph_replay_of_decode_chain_matches_eager(w4):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, a, b in zip(names, outs, want):
+        for name, a, b, ref in zip(names, outs, want, refs):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}: {name} differs from eager"
+            assert_close(host(a), ref, f"replay {rep}: {name}")
         chain()                              # eager launches between replays
         torch.cuda.synchronize()
 
@@ -88,10 +100,17 @@ def test_graph_replay_of_moe_layer_matches_eager(w4):
     tokens, experts, topk, k, n = 96, 12, 4, 512, 256
     wm = [synth.weights(rng, n, k) for _ in range(experts)]
     pq = [w4.quantize(a, 32) for a in wm]
+    oq = [oracle.quantize(a, 32) for a in wm]
     pm, sm = dev(np.stack([a for a, _ in pq])), dev(np.stack([b for _, b in pq]))
-    ids = dev(synth.route_uniform(rng, tokens, experts, topk).choice.astype(np.int32))
-    x = dev(synth.activations(rng, tokens, k))
-    wts = dev(synth.router_weights(rng, tokens, topk))
+    idsn = synth.route_uniform(rng, tokens, experts, topk).choice.astype(np.int32)
+    ids = dev(idsn)
+    xn = synth.activations(rng, tokens, k)
+    x = dev(xn)
+    wtsn = synth.router_weights(rng, tokens, topk)
+    wts = dev(wtsn)
+    out_ref = oracle.moe_layer(xn, idsn, wtsn, np.stack([oracle.pack(a) for a, _ in oq]), np.stack([b for _, b in oq]),
+                               32)
+    offs_ref = oracle.moe_route(idsn, experts)[0]
     offs = torch.empty(experts + 1, dtype=torch.int32, device="cuda")
     tok = torch.empty(tokens * topk, dtype=torch.int32, device="cuda")
     prow = torch.empty((tokens, topk), dtype=torch.int32, device="cuda")
@@ -127,5 +146,7 @@ def test_graph_replay_of_moe_layer_matches_eager(w4):
         torch.cuda.synchronize()
         assert torch.equal(offs, want_offs), f"replay {rep}: offsets differ from eager"
         assert torch.equal(out.view(torch.int16), want_out.view(torch.int16)), f"replay {rep}: layer output differs"
+        assert np.array_equal(host(offs), offs_ref), f"replay {rep}: offsets differ from the oracle's routing"
+        assert_close(host(out), out_ref, f"replay {rep}: MoE layer")
         layer()
         torch.cuda.synchronize()

@@ -136,3 +136,22 @@ def test_grouped_many_experts_work_item_scan(w4):
     y = run_grouped(w4, xs, packed, s, offs, 32)
     y_ref = oracle.grouped_linear(xs, np.stack([oracle.pack(q[e]) for e in range(experts)]), s, offs, 32)
     assert_bit_exact(y, y_ref, f"E={experts} rows={int(offs[-1])}")
+
+
+@pytest.mark.parametrize("group,k", [(32, 2048), (128, 2304)])
+def test_grouped_scales_at_two_byte_offset(w4, group, k):
+    """A scale bank 2 bytes past a 16-byte boundary takes the 2-byte scale loads, bit-exact."""
+    torch = torch_mod()
+    rng = np.random.default_rng(7400 + group)
+    experts, n, counts = 3, 300, [5, 0, 40]
+    q, s = exact_bank(rng, experts, n, k, group)
+    xs = synth.integer_activations(rng, int(sum(counts)), k)
+    offs = offsets_from_counts(counts)
+    flat = torch.zeros(s.size + 8, dtype=torch.float16, device="cuda")
+    sd = flat[1:1 + s.size].view(s.shape)
+    sd.copy_(torch.from_numpy(s))
+    assert sd.data_ptr() % 16 == 2
+    packed = np.stack([w4.pack(q[e]) for e in range(experts)])
+    y = host(w4.grouped_gemm(dev(xs), dev(packed), sd, dev(offs), group))
+    y_ref = oracle.grouped_linear(xs, np.stack([oracle.pack(q[e]) for e in range(experts)]), s, offs, group)
+    assert_bit_exact(y, y_ref, f"offset scales g={group}")

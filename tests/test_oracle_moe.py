@@ -72,3 +72,19 @@ def test_combine_brute_force():
         for c in range(5):
             want = sum(float(w[t, j]) * y_pairs[row[t, j], c] for j in range(3))
             assert abs(out[t, c] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_combine_hand_example():
+    """Two tokens, two slots, values worked out by hand: the combine pairs slot j's
+    router weight with the row that pair_row names for (t, j), not with row j."""
+    # grouped rows (e.g. sorted by expert): row r holds the product of one (token, slot) pair
+    y_pairs = np.array([[1.0, 10.0],     # row 0: (token 1, slot 0)
+                        [2.0, 20.0],     # row 1: (token 0, slot 1)
+                        [3.0, 30.0],     # row 2: (token 0, slot 0)
+                        [4.0, 40.0]])    # row 3: (token 1, slot 1)
+    pair_row = np.array([[2, 1], [0, 3]])
+    w = np.array([[0.5, 0.25], [2.0, -1.0]], np.float32)
+    out = oracle.moe_combine(y_pairs, pair_row, w)
+    # token 0: 0.5 * row 2 + 0.25 * row 1 = (1.5 + 0.5, 15 + 5)
+    # token 1: 2 * row 0 - 1 * row 3 = (2 - 4, 20 - 40)
+    assert out.tolist() == [[2.0, 20.0], [-2.0, -20.0]]

@@ -48,6 +48,7 @@ SIGNATURES = {
     "w4a16_gemv_max_k": (_i64, [_i64, _i32]),
     "w4a16_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "w4a16_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "w4a16_gemm_workspace_status": (ctypes.c_int, [_vp, _sz, _vp]),
     "w4a16_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_gemv_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_moe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -62,7 +63,7 @@ for _name, (_res, _args) in SIGNATURES.items():
     _fn.argtypes = _args
     globals()[_name] = _fn
 
-OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_RANGE = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_RANGE, ERR_TIMEOUT = range(9)
 
 
 class W4A16Error(RuntimeError):
@@ -107,6 +108,11 @@ def unpack(packed: np.ndarray, k: int) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # Device routines (torch tensors on the current HIP device).
+#
+# Every argument is checked before the C call: dtype, contiguity and shape
+# first, then that every tensor lives on the same HIP device.  A mismatch
+# raises ValueError (TypeError for a non-tensor) and nothing is launched, since
+# the library itself can only check pointers, not what they point to.
 # ---------------------------------------------------------------------------
 def _torch():
     import torch
@@ -131,13 +137,74 @@ def _dev_packed(packed):
     return packed
 
 
+def _dtypes(kind):
+    torch = _torch()
+    return {
+        "f16": (torch.float16,),
+        "f32": (torch.float32,),
+        "i32": (torch.int32,),
+        # packed words: int32 or uint32 tensors (the same 32 bits)
+        "u32": tuple(d for d in (torch.int32, getattr(torch, "uint32", None)) if d is not None),
+    }[kind]
+
+
+def _check_tensors(what, specs):
+    """specs: (name, tensor, dtype kind, expected shape or None).  Raises before any launch."""
+    torch = _torch()
+    for name, t, kind, shape in specs:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{what}: {name} must be a torch.Tensor, not {type(t).__name__}")
+        if t.dtype not in _dtypes(kind):
+            raise ValueError(f"{what}: {name} has dtype {t.dtype}, expected {_dtypes(kind)[0]}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: {name} must be contiguous")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{what}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    devs = {t.device for _, t, _, _ in specs}
+    for name, t, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{what}: {name} is on {t.device}; every tensor must be on the HIP device")
+    if len(devs) > 1:
+        raise ValueError(f"{what}: tensors are on different devices {sorted(map(str, devs))}")
+
+
+def _require_tensors(what, **tensors):
+    torch = _torch()
+    for name, t in tensors.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{what}: {name} must be a torch.Tensor, not {type(t).__name__}")
+
+
+def _dense_shapes(what, x, packed, scales, group, rows_per_out=1):
+    """(m, n, k, specs) of a dense product: the 2-D layouts checked, the tensor specs
+    returned for _check_tensors; n counts output columns."""
+    _require_tensors(what, x=x, packed=packed, scales=scales)
+    if x.dim() != 2 or packed.dim() != 2 or scales.dim() != 2:
+        raise ValueError(f"{what}: x, packed and scales must be 2-D")
+    m, k = x.shape
+    if group not in (32, 128) or k % group:
+        raise ValueError(f"{what}: k = {k} must be a multiple of the group size 32 or 128 (got {group})")
+    nw = packed.shape[0]
+    if nw % rows_per_out:
+        raise ValueError(f"{what}: packed must have a multiple of {rows_per_out} rows")
+    specs = [("x", x, "f16", None), ("packed", packed, "u32", (nw, k // 8)),
+             ("scales", scales, "f16", (nw, k // group))]
+    return m, nw // rows_per_out, k, specs
+
+
+def _checked_out(what, specs, out, shape, like):
+    """Check specs plus the output (if given); returns the output, allocated if None."""
+    torch = _torch()
+    _check_tensors(what, specs + ([("out", out, "f16", shape)] if out is not None else []))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float16, device=like.device)
+    return out
+
+
 def gemv(x, packed, scales, group: int, out=None, stream=None):
     """y [m, n] fp16 = x [m, k] . deq(packed, scales)^T, 1 <= m <= 4."""
-    torch = _torch()
-    m, k = x.shape
-    n = packed.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    m, n, k, specs = _dense_shapes("gemv", x, packed, scales, group)
+    out = _checked_out("gemv", specs, out, (m, n), x)
     _check(lib.w4a16_gemv(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k, group, _stream(stream)),
            "w4a16_gemv")
     return out
@@ -152,19 +219,45 @@ def gemm_workspace(m: int, n: int, k: int, group: int, device=None):
     return torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device=device or "cuda")
 
 
+# Workspaces gemm() keeps when the caller passes none: one per (device, stream),
+# grown to the largest size asked for.  Calls on one stream run one after
+# another, which is all a workspace needs; the library leaves it ready for reuse.
+_WORKSPACES = {}
+
+
+def _cached_workspace(m, n, k, group, device, stream_handle):
+    torch = _torch()
+    nbytes = lib.w4a16_gemm_workspace_bytes(m, n, k, group)
+    if nbytes == 0:
+        return None
+    key = (str(device), stream_handle)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() * 4 < nbytes:
+        ws = torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def gemm(x, packed, scales, group: int, out=None, workspace=None, stream=None):
     """y [m, n] fp16 = x [m, k] . deq(packed, scales)^T for any m (fp16 MFMA, fp32 accumulate)."""
-    torch = _torch()
-    m, k = x.shape
-    n = packed.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    m, n, k, specs = _dense_shapes("gemm", x, packed, scales, group)
+    if workspace is not None:
+        specs = specs + [("workspace", workspace, "i32", None)]
+    out = _checked_out("gemm", specs, out, (m, n), x)
+    st = _stream(stream)
     if workspace is None:
-        workspace = gemm_workspace(m, n, k, group, x.device)
+        workspace = _cached_workspace(m, n, k, group, x.device, st.value)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.w4a16_gemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k, group, _ptr(workspace),
-                          ws_bytes, _stream(stream)), "w4a16_gemm")
+                          ws_bytes, st), "w4a16_gemm")
     return out
+
+
+def gemm_workspace_status(workspace, stream=None) -> int:
+    """Status word of a gemm workspace (host-synchronous diagnostic): OK, or ERR_TIMEOUT if a
+    split-K fix-up of an earlier call gave up waiting (its tiles were written as NaN)."""
+    _check_tensors("gemm_workspace_status", [("workspace", workspace, "i32", None)])
+    return lib.w4a16_gemm_workspace_status(_ptr(workspace), workspace.numel() * 4, _stream(stream))
 
 
 def interleave_rows(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
@@ -180,23 +273,33 @@ def interleave_rows(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
 
 def gemv_swiglu(x, packed, scales, group: int, out=None, stream=None):
     """y [m, n] = SiLU(x . Wg^T) * (x . Wu^T), 1 <= m <= 16; packed [2n, k/8] interleaves gate/up rows."""
-    torch = _torch()
-    m, k = x.shape
-    n = packed.shape[0] // 2
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    m, n, k, specs = _dense_shapes("gemv_swiglu", x, packed, scales, group, rows_per_out=2)
+    out = _checked_out("gemv_swiglu", specs, out, (m, n), x)
     _check(lib.w4a16_gemv_swiglu(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k, group, _stream(stream)),
            "w4a16_gemv_swiglu")
     return out
 
 
+def _bank_shapes(what, packed, scales, k, group):
+    _require_tensors(what, packed=packed, scales=scales)
+    if packed.dim() != 3 or scales.dim() != 3:
+        raise ValueError(f"{what}: packed and scales must be [experts, n, ...]")
+    if group not in (32, 128) or k % group:
+        raise ValueError(f"{what}: k = {k} must be a multiple of the group size 32 or 128 (got {group})")
+    experts, n = packed.shape[0], packed.shape[1]
+    return experts, n, [("packed", packed, "u32", (experts, n, k // 8)),
+                        ("scales", scales, "f16", (experts, n, k // group))]
+
+
 def grouped_gemm(x, packed, scales, offsets, group: int, out=None, stream=None):
     """MoE grouped product: rows offsets[e]..offsets[e+1] of x use expert e's weights."""
-    torch = _torch()
+    _require_tensors("grouped_gemm", x=x)
+    if x.dim() != 2:
+        raise ValueError("grouped_gemm: x must be [rows, k]")
     rows, k = x.shape
-    experts, n = packed.shape[0], packed.shape[1]
-    if out is None:
-        out = torch.empty((rows, n), dtype=torch.float16, device=x.device)
+    experts, n, bank = _bank_shapes("grouped_gemm", packed, scales, k, group)
+    out = _checked_out("grouped_gemm", [("x", x, "f16", None)] + bank + [("offsets", offsets, "i32", (experts + 1,))],
+                       out, (rows, n), x)
     _check(lib.w4a16_grouped_gemm(_ptr(x), _ptr(packed), _ptr(scales), _ptr(offsets), _ptr(out), experts, rows,
                                   n, k, group, _stream(stream)), "w4a16_grouped_gemm")
     return out
@@ -204,7 +307,11 @@ def grouped_gemm(x, packed, scales, offsets, group: int, out=None, stream=None):
 
 def moe_route(topk_ids, experts: int, stream=None):
     """Device routing of int32 topk_ids [tokens, topk] -> (offsets [E+1], pair_token [P], pair_row [tokens, topk])."""
+    _require_tensors("moe_route", topk_ids=topk_ids)
     torch = _torch()
+    if topk_ids.dim() != 2:
+        raise ValueError("moe_route: topk_ids must be [tokens, topk]")
+    _check_tensors("moe_route", [("topk_ids", topk_ids, "i32", None)])
     t, topk = topk_ids.shape
     dev_ = topk_ids.device
     offsets = torch.empty(experts + 1, dtype=torch.int32, device=dev_)
@@ -217,12 +324,14 @@ def moe_route(topk_ids, experts: int, stream=None):
 
 def grouped_gemm_gather(x, pair_token, packed, scales, offsets, group: int, out=None, stream=None):
     """Grouped product whose row r reads token pair_token[r] of x [tokens, k]."""
-    torch = _torch()
+    _require_tensors("grouped_gemm_gather", x=x, pair_token=pair_token)
+    if x.dim() != 2 or pair_token.dim() != 1:
+        raise ValueError("grouped_gemm_gather: x must be [tokens, k] and pair_token [rows]")
     tokens, k = x.shape
     rows = pair_token.shape[0]
-    experts, n = packed.shape[0], packed.shape[1]
-    if out is None:
-        out = torch.empty((rows, n), dtype=torch.float16, device=x.device)
+    experts, n, bank = _bank_shapes("grouped_gemm_gather", packed, scales, k, group)
+    out = _checked_out("grouped_gemm_gather", [("x", x, "f16", None), ("pair_token", pair_token, "i32", None)] +
+                       bank + [("offsets", offsets, "i32", (experts + 1,))], out, (rows, n), x)
     _check(lib.w4a16_grouped_gemm_gather(_ptr(x), _ptr(pair_token), _ptr(packed), _ptr(scales), _ptr(offsets),
                                          _ptr(out), experts, rows, tokens, n, k, group, _stream(stream)),
            "w4a16_grouped_gemm_gather")
@@ -231,16 +340,18 @@ def grouped_gemm_gather(x, pair_token, packed, scales, offsets, group: int, out=
 
 def moe_combine(y_pairs, pair_row, weights, out=None, stream=None):
     """out [tokens, n] = sum_j weights[t, j] * y_pairs[pair_row[t, j]] (weights fp32 [tokens, topk])."""
-    torch = _torch()
+    _require_tensors("moe_combine", y_pairs=y_pairs, pair_row=pair_row, weights=weights)
+    if y_pairs.dim() != 2 or pair_row.dim() != 2:
+        raise ValueError("moe_combine: y_pairs must be [rows, n] and pair_row [tokens, topk]")
     tokens, topk = pair_row.shape
     rows, n = y_pairs.shape
-    if out is None:
-        out = torch.empty((tokens, n), dtype=torch.float16, device=y_pairs.device)
+    out = _checked_out("moe_combine", [("y_pairs", y_pairs, "f16", None), ("pair_row", pair_row, "i32", None),
+                                       ("weights", weights, "f32", (tokens, topk))], out, (tokens, n), y_pairs)
     _check(lib.w4a16_moe_combine(_ptr(y_pairs), _ptr(pair_row), _ptr(weights), _ptr(out), tokens, topk, rows, n,
                                  _stream(stream)), "w4a16_moe_combine")
     return out
 
 
 __all__ = ["lib", "LIB_PATH", "SIGNATURES", "W4A16Error", "quantize", "pack", "unpack", "gemv", "gemm",
-           "gemm_workspace", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
+           "gemm_workspace", "gemm_workspace_status", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
            "grouped_gemm_gather", "moe_combine"] + list(SIGNATURES)

@@ -4,7 +4,7 @@
 // Every check runs on the host before anything is launched, in a fixed order
 // (group, shape, null, alignment, size limits, device), so a CPU-only process
 // can exercise every validation error without touching a GPU.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <atomic>
 #include <cstdint>
@@ -59,6 +59,14 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 // Experts the routing kernel counts in LDS (one int per expert beside 4 KB).
 constexpr int32_t kMaxRouteExperts = 32768;
 
+// A bank of `experts` packed [n, k/8] weight tensors stays below the buffer
+// limit (n, k <= 2^30 already; the product is bounded before it is formed).
+bool bank_fits(int64_t experts, int64_t n, int64_t k) {
+  const int64_t per = n * (k / 2);
+  if (per >= kMaxBufferBytes) return false;
+  return per == 0 || experts < kMaxBufferBytes / per;
+}
+
 int common_dense_checks(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
                         int64_t m, int64_t n, int64_t k, int32_t group) {
   if (!valid_group(group)) return W4A16_ERR_GROUP;
@@ -74,7 +82,8 @@ int common_dense_checks(const uint16_t* x, const uint32_t* packed, const uint16_
   return W4A16_OK;
 }
 
-int status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+w4a16_status status_of(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+w4a16_status as_status(int s) { return static_cast<w4a16_status>(s); }
 
 // Which kernels w4a16_gemm runs: up to 32 rows the product is a weight stream
 // (m <= 4: the decode GEMV kernels while their plan fits; 5..32: the
@@ -88,10 +97,21 @@ GemmPath gemm_path(int64_t m, int64_t n, int64_t k, int32_t group, const DeviceI
     size_t mlds = 0;
     if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, dev, &mb, &mlds)) return GemmPath::kGemv;
     if (w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev).ok) return GemmPath::kGemv;
-    return GemmPath::kTiled;
   }
   if (m <= 32 && w4a16::gemm_skinny_fits((int)(m < 16 ? m : 16), (int)n, (int)k, dev)) return GemmPath::kSkinny;
   return GemmPath::kTiled;
+}
+
+// The weight-streaming kernel, one pass per 16 rows (k > 0, arguments checked).
+int skinny_passes(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+                  int64_t n, int64_t k, int32_t group, const DeviceInfo& dev, hipStream_t st) {
+  for (int64_t m0 = 0; m0 < m; m0 += 16) {
+    const int mm = (int)(m - m0 < 16 ? m - m0 : 16);
+    const hipError_t e = w4a16::launch_gemm_skinny(x + m0 * k, packed, scales, y + m0 * n, mm, (int)n, (int)k,
+                                                   group, dev, st);
+    if (e != hipSuccess) return W4A16_ERR_HIP;
+  }
+  return W4A16_OK;
 }
 
 // The decode GEMV kernels for 1 <= m <= 4 (k > 0, arguments already checked).
@@ -125,6 +145,7 @@ const char* w4a16_status_str(int status) {
     case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE: workspace missing or too small";
     case W4A16_ERR_HIP: return "W4A16_ERR_HIP: HIP runtime error";
     case W4A16_ERR_RANGE: return "W4A16_ERR_RANGE: value out of range";
+    case W4A16_ERR_TIMEOUT: return "W4A16_ERR_TIMEOUT: a split-K fix-up gave up waiting; outputs were written as NaN";
     default: return "W4A16: unknown status";
   }
 }
@@ -136,18 +157,22 @@ int64_t w4a16_gemv_max_k(int64_t m, int32_t group) {
   return w4a16::gemv_max_k((int)m, group, dev);
 }
 
-int w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
-               int64_t n, int64_t k, int32_t group, void* stream) {
+w4a16_status w4a16_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+               int64_t n, int64_t k, int32_t group, w4a16_stream_t stream) {
   if (valid_group(group) && m > 4) return W4A16_ERR_SHAPE;
   int c = common_dense_checks(x, packed, scales, y, m, n, k, group);
   if (c < 0) return W4A16_OK;
-  if (c != W4A16_OK) return c;
+  if (c != W4A16_OK) return as_status(c);
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
   const int r = gemv_dispatch(x, packed, scales, y, m, n, k, group, dev, st);
-  return r < 0 ? W4A16_ERR_SHAPE : r;
+  if (r >= 0) return as_status(r);
+  // k too long for the LDS-staged decode kernels: the weight-streaming kernel
+  // stages the activations in chunks and takes any k
+  if (!w4a16::gemm_skinny_fits((int)m, (int)n, (int)k, dev)) return W4A16_ERR_SHAPE;
+  return as_status(skinny_passes(x, packed, scales, y, m, n, k, group, dev, st));
 }
 
 size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group) {
@@ -159,11 +184,12 @@ size_t w4a16_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t group
   return w4a16::gemm_workspace_bytes(m, n, k, group, dev);
 }
 
-int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
-               int64_t n, int64_t k, int32_t group, void* workspace, size_t workspace_bytes, void* stream) {
+w4a16_status w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+               int64_t n, int64_t k, int32_t group, void* workspace, size_t workspace_bytes,
+               w4a16_stream_t stream) {
   int c = common_dense_checks(x, packed, scales, y, m, n, k, group);
   if (c < 0) return W4A16_OK;
-  if (c != W4A16_OK) return c;
+  if (c != W4A16_OK) return as_status(c);
   if (workspace && !aligned(workspace, 16)) return W4A16_ERR_ALIGN;
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
@@ -172,32 +198,42 @@ int w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales
   const GemmPath path = gemm_path(m, n, k, group, dev);
   if (path == GemmPath::kGemv) {
     const int r = gemv_dispatch(x, packed, scales, y, m, n, k, group, dev, st);
-    return r < 0 ? W4A16_ERR_SHAPE : r;   // not reached: gemm_path checked the plan
+    return as_status(r < 0 ? W4A16_ERR_SHAPE : r);   // not reached: gemm_path checked the plan
   }
-  if (path == GemmPath::kSkinny) {
-    // one pass per 16 rows (two passes beat the 128-row GEMM tiles up to 32 rows)
-    for (int64_t m0 = 0; m0 < m; m0 += 16) {
-      const int mm = (int)(m - m0 < 16 ? m - m0 : 16);
-      const hipError_t e = w4a16::launch_gemm_skinny(x + m0 * k, packed, scales, y + m0 * n, mm, (int)n, (int)k,
-                                                     group, dev, st);
-      if (e != hipSuccess) return W4A16_ERR_HIP;
-    }
-    return W4A16_OK;
-  }
+  // one pass per 16 rows (two passes beat the 128-row GEMM tiles up to 32 rows)
+  if (path == GemmPath::kSkinny) return as_status(skinny_passes(x, packed, scales, y, m, n, k, group, dev, st));
   const size_t need = w4a16::gemm_workspace_bytes(m, n, k, group, dev);
   if (need && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
   return status_of(w4a16::launch_gemm(x, packed, scales, y, (int)m, (int)n, (int)k, group,
                                       need ? workspace : nullptr, dev, st));
 }
 
-int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
-                      int64_t n, int64_t k, int32_t group, void* stream) {
+w4a16_status w4a16_gemm_workspace_status(void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
+  if (!workspace) return W4A16_ERR_NULL;
+  if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;
+  if (workspace_bytes < w4a16::kWorkspaceHeader) return W4A16_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  const uint32_t zero = 0;
+  // synchronous: read the word after the stream's earlier work, then clear it
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess) return W4A16_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return W4A16_ERR_HIP;
+  if (word != 0) {
+    if (hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, st) != hipSuccess) return W4A16_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return W4A16_ERR_HIP;
+    return W4A16_ERR_TIMEOUT;
+  }
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
+                      int64_t n, int64_t k, int32_t group, w4a16_stream_t stream) {
   if (valid_group(group) && m > 16) return W4A16_ERR_SHAPE;
   if (n > kMaxDim / 2) return W4A16_ERR_SHAPE;
   // the weights have 2n rows; y has n columns (checked as part of the 2n-column bound)
   int c = common_dense_checks(x, packed, scales, y, m, 2 * n, k, group);
   if (c < 0) return W4A16_OK;
-  if (c != W4A16_OK) return c;
+  if (c != W4A16_OK) return as_status(c);
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -218,9 +254,9 @@ int w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const uint16_t*
   return status_of(w4a16::launch_swiglu_skinny(x, packed, scales, y, (int)m, (int)n, (int)k, group, dev, st));
 }
 
-int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
+w4a16_status w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
                        uint16_t* y, int32_t num_experts, int64_t rows, int64_t n, int64_t k, int32_t group,
-                       void* stream) {
+                       w4a16_stream_t stream) {
   if (!valid_group(group)) return W4A16_ERR_GROUP;
   if (num_experts < 0 || rows < 0 || n < 0 || k < 0 || k % group) return W4A16_ERR_SHAPE;
   if (rows > kMaxDim || n > kMaxDim || k > kMaxDim) return W4A16_ERR_SHAPE;
@@ -231,7 +267,7 @@ int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
   if (!aligned(y, 16) || !aligned(offsets, 4) ||
       (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2))))
     return W4A16_ERR_ALIGN;
-  if ((int64_t)num_experts * n * (k / 2) >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (!bank_fits(num_experts, n, k)) return W4A16_ERR_SHAPE;
   if (2 * rows * k >= kMaxBufferBytes || 2 * rows * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
@@ -241,9 +277,10 @@ int w4a16_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
                                               (int)k, group, dev, st));
 }
 
-int w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
+w4a16_status w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
                               const uint16_t* scales, const int32_t* offsets, uint16_t* y, int32_t num_experts,
-                              int64_t rows, int64_t tokens, int64_t n, int64_t k, int32_t group, void* stream) {
+                              int64_t rows, int64_t tokens, int64_t n, int64_t k, int32_t group,
+                              w4a16_stream_t stream) {
   if (!valid_group(group)) return W4A16_ERR_GROUP;
   if (num_experts < 0 || rows < 0 || tokens < 0 || n < 0 || k < 0 || k % group) return W4A16_ERR_SHAPE;
   if (rows > kMaxDim || tokens > kMaxDim || n > kMaxDim || k > kMaxDim) return W4A16_ERR_SHAPE;
@@ -254,7 +291,7 @@ int w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, cons
   if (!aligned(y, 16) || !aligned(offsets, 4) ||
       (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(pair_token, 4))))
     return W4A16_ERR_ALIGN;
-  if ((int64_t)num_experts * n * (k / 2) >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  if (!bank_fits(num_experts, n, k)) return W4A16_ERR_SHAPE;
   if (2 * tokens * k >= kMaxBufferBytes || 2 * rows * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
   DeviceInfo dev;
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
@@ -264,10 +301,10 @@ int w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, cons
                                                      num_experts, (int)rows, (int)n, (int)k, group, dev, st));
 }
 
-int w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts, int32_t* offsets,
-                    int32_t* pair_token, int32_t* pair_row, void* stream) {
+w4a16_status w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts, int32_t* offsets,
+                    int32_t* pair_token, int32_t* pair_row, w4a16_stream_t stream) {
   if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > kMaxRouteExperts) return W4A16_ERR_SHAPE;
-  if (tokens * topk >= ((int64_t)1 << 31)) return W4A16_ERR_SHAPE;
+  if (tokens > kMaxDim || tokens * topk >= ((int64_t)1 << 31)) return W4A16_ERR_SHAPE;
   if (!offsets) return W4A16_ERR_NULL;
   if (tokens > 0 && (!topk_ids || !pair_token || !pair_row)) return W4A16_ERR_NULL;
   if (!aligned(offsets, 4) || (tokens > 0 && (!aligned(topk_ids, 4) || !aligned(pair_token, 4) ||
@@ -280,8 +317,8 @@ int w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32
                                            pair_row, dev, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
-                      int64_t tokens, int32_t topk, int64_t rows, int64_t n, void* stream) {
+w4a16_status w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
+                      int64_t tokens, int32_t topk, int64_t rows, int64_t n, w4a16_stream_t stream) {
   if (tokens < 0 || topk < 1 || rows < 0 || n < 0) return W4A16_ERR_SHAPE;
   if (tokens > kMaxDim || rows > kMaxDim || n > kMaxDim || tokens * topk >= ((int64_t)1 << 31)) return W4A16_ERR_SHAPE;
   if (2 * rows * n >= kMaxBufferBytes || 2 * tokens * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;

@@ -45,6 +45,7 @@
 // partial sum is exact, so such inputs give bit-exact results.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 #include "mfma_operands.hpp"
 
 namespace w4a16 {
@@ -179,7 +180,8 @@ __global__ void __launch_bounds__(kThreads)
 gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
             const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
             int M, int N, int K, int tiles_m, int tiles_n, int iters, int rounds, int sk_tiles, int nsk,
-            float* __restrict__ partials, uint32_t* __restrict__ flags, uint32_t* __restrict__ counters) {
+            float* __restrict__ partials, uint32_t* __restrict__ flags, uint32_t* __restrict__ counters,
+            uint32_t* __restrict__ status) {
   constexpr int kGroups = BK / G;            // scale groups per K step (1 or 4)
   constexpr int kSBytes = SALIGN ? 0 : BN * kGroups * 4;       // per-stage scales (unaligned case)
   constexpr int kStage = kStageBytes + kSBytes;
@@ -580,7 +582,11 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
       if (++spins == kSpinLimit) { failed_poll = true; break; }
     }
     (void)pending;
-    if (lane == 0) give_up = failed_poll ? 1 : 0;
+    if (lane == 0) {
+      give_up = failed_poll ? 1 : 0;
+      // recorded for the caller (w4a16_gemm_workspace_status)
+      if (failed_poll) __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __syncthreads();
   const bool failed = give_up != 0;
@@ -643,18 +649,23 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int, const DeviceInfo& dev) {
   const GemmPlan p = gemm_plan((int)m, (int)n, (int)k, dev);
   if (p.sk_tiles == 0) return 0;
-  // two partial slots and two flags per workgroup, one counter per stream-K tile slot
-  return 2 * (size_t)p.wgs * kPartialBytes + 3 * (size_t)p.wgs * sizeof(uint32_t);
+  // the status word (kWorkspaceHeader bytes), two partial slots and two flags per
+  // workgroup, one counter per stream-K tile slot
+  return kWorkspaceHeader + 2 * (size_t)p.wgs * kPartialBytes + 3 * (size_t)p.wgs * sizeof(uint32_t);
 }
 
 hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                        int n, int k, int group, void* workspace, const DeviceInfo& dev, hipStream_t stream) {
   const GemmPlan p = gemm_plan(m, n, k, dev);
-  float* partials = static_cast<float*>(workspace);
+  float* partials = nullptr;
   uint32_t* flags = nullptr;
   uint32_t* counters = nullptr;
+  uint32_t* status = nullptr;
   if (workspace) {
-    flags = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + 2 * (size_t)p.wgs * kPartialBytes);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    status = reinterpret_cast<uint32_t*>(ws);
+    partials = reinterpret_cast<float*>(ws + kWorkspaceHeader);
+    flags = reinterpret_cast<uint32_t*>(ws + kWorkspaceHeader + 2 * (size_t)p.wgs * kPartialBytes);
     counters = flags + 2 * (size_t)p.wgs;
   }
   const bool tail = k % BK != 0;
@@ -663,10 +674,8 @@ hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t
               : tail       ? gemm_kernel<32, true, false>
               : salign     ? gemm_kernel<32, false, true>
                            : gemm_kernel<32, false, false>;
-  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL(kern, dim3(p.wgs), dim3(kThreads), 0, stream, x, packed, scales, y, m, n, k, p.tiles_m,
-                     p.tiles_n, p.iters, p.rounds, p.sk_tiles, p.nsk, partials, flags, counters);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(p.wgs), dim3(kThreads), 0, stream, x, packed, scales, y, m, n, k, p.tiles_m,
+                       p.tiles_n, p.iters, p.rounds, p.sk_tiles, p.nsk, partials, flags, counters, status);
 }
 
 }  // namespace w4a16

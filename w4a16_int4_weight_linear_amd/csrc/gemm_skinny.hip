@@ -28,6 +28,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 #include "mfma_operands.hpp"
 
 namespace w4a16 {
@@ -265,10 +266,8 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
 template <int G, bool ALIGNED, bool SWIGLU>
 hipError_t launch_ga(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m, int n,
                      int k, int blocks, int units, hipStream_t stream) {
-  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL((gemm_skinny_kernel<G, ALIGNED, SWIGLU>), dim3(blocks), dim3(kThreads), 0, stream, x, packed,
-                     scales, y, m, n, k, units / blocks, units % blocks);
-  return hipGetLastError();
+  return launch_kernel(gemm_skinny_kernel<G, ALIGNED, SWIGLU>, dim3(blocks), dim3(kThreads), 0, stream, x, packed,
+                       scales, y, m, n, k, units / blocks, units % blocks);
 }
 
 // n weight rows in units of `unit` rows (2: gate/up pairs); returns the grid.
@@ -290,20 +289,22 @@ hipError_t launch_s(const uint16_t* x, const uint32_t* packed, const uint16_t* s
   const int g = skinny_grid(n, unit, dev);
   const int units = n / unit;
   const int spr = k / group;
+  // one vector load per row brings a line's scales when every scale row is
+  // 16-byte (g32) or 4-byte (g128) aligned in memory
+  const uintptr_t sp = reinterpret_cast<uintptr_t>(scales);
   if (group == 32)
-    return spr % 8 == 0 ? launch_ga<32, true, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream)
-                        : launch_ga<32, false, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream);
-  return spr % 2 == 0 ? launch_ga<128, true, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream)
-                      : launch_ga<128, false, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream);
+    return spr % 8 == 0 && (sp & 15) == 0 ? launch_ga<32, true, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream)
+                                          : launch_ga<32, false, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream);
+  return spr % 2 == 0 && (sp & 3) == 0 ? launch_ga<128, true, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream)
+                                       : launch_ga<128, false, SWIGLU>(x, packed, scales, y, m, n, k, g, units, stream);
 }
 
 }  // namespace
 
 bool gemm_skinny_fits(int m, int n, int k, const DeviceInfo& dev) {
-  (void)k;
-  return m >= 5 && m <= kRows && n > 0 && dev.max_lds >= (size_t)kLds;
+  (void)k;   // any k: the activations are staged in chunks
+  return m >= 1 && m <= kRows && n > 0 && dev.max_lds >= (size_t)kLds;
 }
-// (The kernel itself takes any 1 <= m <= 16; the caller slices larger m.)
 
 hipError_t launch_gemm_skinny(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                               int n, int k, int group, const DeviceInfo& dev, hipStream_t stream) {

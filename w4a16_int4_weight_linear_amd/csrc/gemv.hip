@@ -58,6 +58,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 
 namespace w4a16 {
 namespace {
@@ -117,7 +118,7 @@ template <int M, bool GATED>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
             const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
-            int n, int k, int gshift, int rows_base, int rows_extra) {
+            int n, int k, int gshift, int rows_base, int rows_extra, uint32_t sc_shift) {
   // rows_base / rows_extra count row units: single rows, or gate/up row pairs.
   constexpr int kUnit = GATED ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -150,10 +151,12 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   const GemvLayout L = gemv_layout(M, C, spr, kUnit * (rows_base + (rows_extra ? 1 : 0)));
 
   // ---- staging loads (activations, scales), issued before the weight stream ----
-  const uint32_t sc_begin = (uint32_t)wg_r0 * (uint32_t)spr * 2u;
+  // `scales` is rounded down to 16 bytes by the launcher and sc_shift bytes
+  // added back here, so the 16-byte staging loads are aligned in memory
+  const uint32_t sc_begin = (uint32_t)wg_r0 * (uint32_t)spr * 2u + sc_shift;
   const uint32_t sc_a0 = sc_begin & ~15u;
   const uint32_t sc_chunks = (sc_begin - sc_a0 + (uint32_t)nr * (uint32_t)spr * 2u + kScaleSlack + 15u) >> 4;
-  const uint32_t sc_bytes = (uint32_t)n * (uint32_t)spr * 2u;
+  const uint32_t sc_bytes = (uint32_t)n * (uint32_t)spr * 2u + sc_shift;
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, sc_bytes);
   const int pairs = C * M;                        // (chunk, activation row) pairs
   u32x4 a[2][4];
@@ -527,10 +530,10 @@ hipError_t launch_gemv_m(const uint16_t* x, const uint32_t* packed, const uint16
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   const int gshift = group == 128 ? 2 : 0;   // log2(group / 32)
-  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL((gemv_kernel<M, GATED>), dim3(plan.blocks), dim3(kGemvThreads), plan.lds, stream, x, packed, scales, y,
-                     n, k, gshift, plan.rows_base, plan.rows_extra);
-  return hipGetLastError();
+  const uint32_t sc_shift = (uint32_t)(reinterpret_cast<uintptr_t>(scales) & 15u);
+  const uint16_t* sc_aligned = reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(scales) - sc_shift);
+  return launch_kernel(gemv_kernel<M, GATED>, dim3(plan.blocks), dim3(kGemvThreads), plan.lds, stream, x, packed,
+                       sc_aligned, y, n, k, gshift, plan.rows_base, plan.rows_extra, sc_shift);
 }
 
 size_t plan_lds(int m, int units, int k, int group, int blocks, int unit) {

@@ -27,6 +27,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 #include "mfma_operands.hpp"
 
 namespace w4a16 {
@@ -264,22 +265,25 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* s
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
-  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
   const int units = GATED ? n / 2 : n;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, stream, x, packed, scales, y, n, k, units / blocks,
-                     units % blocks);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(blocks), dim3(kThreads), lds, stream, x, packed, scales, y, n, k, units / blocks,
+                       units % blocks);
 }
 
 template <int M, bool GATED>
 hipError_t launch_g(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
                     int group, int blocks, size_t lds, const DeviceInfo& dev, hipStream_t stream) {
   const int spr = k / group;
+  // one vector load per row brings a line's scales when every scale row is
+  // 16-byte (g32) or 4-byte (g128) aligned in memory
+  const uintptr_t sp = reinterpret_cast<uintptr_t>(scales);
   if (group == 32)
-    return spr % 8 == 0 ? launch_m<M, 32, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
-                        : launch_m<M, 32, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
-  return spr % 2 == 0 ? launch_m<M, 128, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
-                      : launch_m<M, 128, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
+    return spr % 8 == 0 && (sp & 15) == 0
+               ? launch_m<M, 32, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
+               : launch_m<M, 32, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
+  return spr % 2 == 0 && (sp & 3) == 0
+             ? launch_m<M, 128, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
+             : launch_m<M, 128, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
 }
 
 }  // namespace

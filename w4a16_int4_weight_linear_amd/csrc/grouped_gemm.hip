@@ -35,6 +35,7 @@
 //   copy of the activations is never written.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 #include "mfma_operands.hpp"
 
 #include <type_traits>
@@ -410,13 +411,14 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* pair_token, int x_ro
   const int64_t blocks = items * bands;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int spr = k / group;
-  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
   const dim3 grid((unsigned)blocks), block(kThreads);
-  auto kern = group == 32 ? (spr % 8 == 0 ? grouped_gemm_kernel<32, true> : grouped_gemm_kernel<32, false>)
-                          : (spr % 2 == 0 ? grouped_gemm_kernel<128, true> : grouped_gemm_kernel<128, false>);
-  hipLaunchKernelGGL(kern, grid, block, 0, stream, x, packed, scales, offsets, y, experts, n, k, rows, bands,
-                     pair_token, x_rows);
-  return hipGetLastError();
+  // one vector load per row brings a step's scales when every scale row is
+  // 16-byte (g32) or 4-byte (g128) aligned in memory
+  const uintptr_t sp = reinterpret_cast<uintptr_t>(scales);
+  auto kern = group == 32 ? (spr % 8 == 0 && (sp & 15) == 0 ? grouped_gemm_kernel<32, true> : grouped_gemm_kernel<32, false>)
+                          : (spr % 2 == 0 && (sp & 3) == 0 ? grouped_gemm_kernel<128, true> : grouped_gemm_kernel<128, false>);
+  return launch_kernel(kern, grid, block, 0, stream, x, packed, scales, offsets, y, experts, n, k, rows, bands,
+                       pair_token, x_rows);
 }
 
 }  // namespace

@@ -65,7 +65,7 @@ bool valid_group(int32_t g) { return g == 32 || g == 128; }
 
 extern "C" {
 
-int w4a16_quantize(const float* w, int64_t n, int64_t k, int32_t group, uint32_t* packed,
+w4a16_status w4a16_quantize(const float* w, int64_t n, int64_t k, int32_t group, uint32_t* packed,
                    uint16_t* scales) {
   if (!valid_group(group)) return W4A16_ERR_GROUP;
   if (n < 0 || k < 0 || k % group) return W4A16_ERR_SHAPE;
@@ -111,7 +111,7 @@ int w4a16_quantize(const float* w, int64_t n, int64_t k, int32_t group, uint32_t
   return W4A16_OK;
 }
 
-int w4a16_pack(const int8_t* q, int64_t n, int64_t k, uint32_t* packed) {
+w4a16_status w4a16_pack(const int8_t* q, int64_t n, int64_t k, uint32_t* packed) {
   if (n < 0 || k < 0 || k % 8) return W4A16_ERR_SHAPE;
   if (n == 0 || k == 0) return W4A16_OK;
   if (!q || !packed) return W4A16_ERR_NULL;
@@ -126,7 +126,7 @@ int w4a16_pack(const int8_t* q, int64_t n, int64_t k, uint32_t* packed) {
   return W4A16_OK;
 }
 
-int w4a16_unpack(const uint32_t* packed, int64_t n, int64_t k, int8_t* q) {
+w4a16_status w4a16_unpack(const uint32_t* packed, int64_t n, int64_t k, int8_t* q) {
   if (n < 0 || k < 0 || k % 8) return W4A16_ERR_SHAPE;
   if (n == 0 || k == 0) return W4A16_OK;
   if (!q || !packed) return W4A16_ERR_NULL;

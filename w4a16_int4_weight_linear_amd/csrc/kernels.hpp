@@ -4,7 +4,7 @@
 // argument before calling them) and return the HIP error of the launch.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -52,6 +52,9 @@ hipError_t launch_swiglu_skinny(const uint16_t* x, const uint32_t* packed, const
                                 int m, int n_out, int k, int group, const DeviceInfo& dev, hipStream_t stream);
 
 // ---- prefill GEMM (gemm.hip) ----
+// The workspace starts with a status word (non-zero after a stream-K fix-up
+// gave up waiting), padded to kWorkspaceHeader bytes; the partial tiles follow.
+constexpr size_t kWorkspaceHeader = 256;
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int group, const DeviceInfo& dev);
 hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
                        int m, int n, int k, int group, void* workspace, const DeviceInfo& dev,

@@ -1,6 +1,7 @@
 // misc.hip -- y = 0 for the empty sum (k == 0).
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 
 namespace w4a16 {
 namespace {
@@ -14,8 +15,6 @@ hipError_t launch_zero_fill(uint16_t* y, size_t count, hipStream_t stream) {
   if (count == 0) return hipSuccess;
   size_t blocks = (count + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, count);
-  return hipGetLastError();
+  return launch_kernel(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, count);
 }
 }  // namespace w4a16

@@ -21,6 +21,7 @@
 //   to fp16.
 #include "device.hpp"
 #include "kernels.hpp"
+#include "launch.hpp"
 
 namespace w4a16 {
 namespace {
@@ -171,10 +172,8 @@ hipError_t launch_moe_route(const int32_t* ids, int pairs, int topk, int experts
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
     if (e != hipSuccess) return e;
   }
-  (void)hipGetLastError();   // drop an error left by an earlier HIP call of the process
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), lds, stream, ids, pairs, topk, experts, offsets,
-                     pair_token, pair_row);
-  return hipGetLastError();
+  return launch_kernel(moe_route_kernel, dim3(1), dim3(kRouteThreads), lds, stream, ids, pairs, topk, experts, offsets,
+                       pair_token, pair_row);
 }
 
 hipError_t launch_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
@@ -182,10 +181,8 @@ hipError_t launch_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, 
   const int64_t threads = (int64_t)tokens * ((n + 7) / 8);
   const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y_pairs, pair_row, weights,
-                     out, tokens, topk, n, rows);
-  return hipGetLastError();
+  return launch_kernel(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y_pairs, pair_row, weights,
+                       out, tokens, topk, n, rows);
 }
 
 }  // namespace w4a16
