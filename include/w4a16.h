@@ -149,6 +149,25 @@ w4a16_status w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_
                         void* workspace, size_t workspace_bytes, w4a16_stream_t stream);
 
 /*
+ * w4a16_gemm for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same product, the
+ * same kernels and result bars, with no workspace argument.  The split-K
+ * partial tiles go to a scratch array of the library itself (64 MiB + 3 KiB:
+ * room for 256 persistent workgroups, one per CU of an MI355X), which each GPU
+ * the library runs on holds from first use until the process ends.  Calls no
+ * allocating routine.  A device whose plan needs more (more than 256 CUs)
+ * gets W4A16_ERR_WORKSPACE.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (concurrent streams, or several host threads)
+ * race and must not be issued; calls in order on one stream are fine.  Each
+ * call clears the scratch's flags with a fill kernel before its product runs.
+ * A split-K fix-up that gives up writes NaN, as in w4a16_gemm (its status
+ * word is not readable here).
+ */
+w4a16_status w4a16_gemm_noalloc(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                                uint16_t* y, int64_t m, int64_t n, int64_t k, int32_t group,
+                                w4a16_stream_t stream);
+
+/*
  * Diagnostic, not for the hot path: waits for the work queued on `stream`,
  * then reads the status word at the start of a w4a16_gemm workspace (device
  * pointer, at least 256 bytes).  Returns W4A16_ERR_TIMEOUT, and clears the

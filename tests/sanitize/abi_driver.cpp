@@ -99,6 +99,11 @@ static void device_validation() {
   EXPECT(w4a16_gemm(x, p, s, y, INT64_MAX, INT64_MAX, INT64_MAX, 128, nullptr, 0, nullptr) == W4A16_ERR_SHAPE);
   EXPECT(w4a16_gemm(x, p, s, y, 600, 64, 128, 128, nullptr, 0, nullptr) == W4A16_ERR_HIP);
   EXPECT(w4a16_gemm_workspace_bytes(INT64_MAX, 64, 128, 128) == 0);
+  EXPECT(w4a16_gemm_noalloc(x, p, s, y, 8, 64, 128, 16, nullptr) == W4A16_ERR_GROUP);
+  EXPECT(w4a16_gemm_noalloc(x, p, s, nullptr, 8, 64, 128, 128, nullptr) == W4A16_ERR_NULL);
+  EXPECT(w4a16_gemm_noalloc(x, p, s, F<uint16_t>(2), 8, 64, 128, 128, nullptr) == W4A16_ERR_ALIGN);
+  EXPECT(w4a16_gemm_noalloc(nullptr, nullptr, nullptr, nullptr, 0, 64, 128, 128, nullptr) == W4A16_OK);
+  EXPECT(w4a16_gemm_noalloc(x, p, s, y, 600, 64, 128, 128, nullptr) == W4A16_ERR_HIP);
   EXPECT(w4a16_gemm_workspace_status(nullptr, 4096, nullptr) == W4A16_ERR_NULL);
   EXPECT(w4a16_gemm_workspace_status(fake(4), 4096, nullptr) == W4A16_ERR_ALIGN);
   EXPECT(w4a16_gemm_workspace_status(fake(), 16, nullptr) == W4A16_ERR_WORKSPACE);

@@ -19,6 +19,8 @@ hipError_t launch_gemm_skinny(const uint16_t*, const uint32_t*, const uint16_t*,
 hipError_t launch_swiglu_skinny(const uint16_t*, const uint32_t*, const uint16_t*, uint16_t*, int, int, int, int,
                                 const DeviceInfo&, hipStream_t) { return hipErrorNoDevice; }
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, int, const DeviceInfo&) { return 0; }
+hipError_t gemm_scratch(const DeviceInfo&, void**, size_t*) { return hipErrorNoDevice; }
+size_t gemm_workspace_flags_offset(int64_t, int64_t, int64_t, const DeviceInfo&) { return 0; }
 hipError_t launch_gemm(const uint16_t*, const uint32_t*, const uint16_t*, uint16_t*, int, int, int, int, void*,
                        const DeviceInfo&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_grouped_gemm(const uint16_t*, const uint32_t*, const uint16_t*, const int32_t*, uint16_t*, int,

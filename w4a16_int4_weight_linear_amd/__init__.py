@@ -49,6 +49,7 @@ SIGNATURES = {
     "w4a16_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "w4a16_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_gemm_workspace_status": (ctypes.c_int, [_vp, _sz, _vp]),
+    "w4a16_gemm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_gemv_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_moe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -253,6 +254,16 @@ def gemm(x, packed, scales, group: int, out=None, workspace=None, stream=None):
     return out
 
 
+def gemm_noalloc(x, packed, scales, group: int, out=None, stream=None):
+    """gemm without a workspace: the library's own scratch holds the split-K partials
+    (calls that overlap on one GPU race; allocates nothing when `out` is given)."""
+    m, n, k, specs = _dense_shapes("gemm_noalloc", x, packed, scales, group)
+    out = _checked_out("gemm_noalloc", specs, out, (m, n), x)
+    _check(lib.w4a16_gemm_noalloc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k, group, _stream(stream)),
+           "w4a16_gemm_noalloc")
+    return out
+
+
 def gemm_workspace_status(workspace, stream=None) -> int:
     """Status word of a gemm workspace (host-synchronous diagnostic): OK, or ERR_TIMEOUT if a
     split-K fix-up of an earlier call gave up waiting (its tiles were written as NaN)."""
@@ -353,5 +364,5 @@ def moe_combine(y_pairs, pair_row, weights, out=None, stream=None):
 
 
 __all__ = ["lib", "LIB_PATH", "SIGNATURES", "W4A16Error", "quantize", "pack", "unpack", "gemv", "gemm",
-           "gemm_workspace", "gemm_workspace_status", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
+           "gemm_workspace", "gemm_workspace_status", "gemm_noalloc", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
            "grouped_gemm_gather", "moe_combine"] + list(SIGNATURES)

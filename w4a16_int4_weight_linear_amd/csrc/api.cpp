@@ -208,6 +208,38 @@ w4a16_status w4a16_gemm(const uint16_t* x, const uint32_t* packed, const uint16_
                                       need ? workspace : nullptr, dev, st));
 }
 
+w4a16_status w4a16_gemm_noalloc(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
+                                int64_t m, int64_t n, int64_t k, int32_t group, w4a16_stream_t stream) {
+  int c = common_dense_checks(x, packed, scales, y, m, n, k, group);
+  if (c < 0) return W4A16_OK;
+  if (c != W4A16_OK) return as_status(c);
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));
+  const GemmPath path = gemm_path(m, n, k, group, dev);
+  if (path == GemmPath::kGemv) {
+    const int r = gemv_dispatch(x, packed, scales, y, m, n, k, group, dev, st);
+    return as_status(r < 0 ? W4A16_ERR_SHAPE : r);
+  }
+  if (path == GemmPath::kSkinny) return as_status(skinny_passes(x, packed, scales, y, m, n, k, group, dev, st));
+  const size_t need = w4a16::gemm_workspace_bytes(m, n, k, group, dev);
+  if (need == 0)
+    return status_of(w4a16::launch_gemm(x, packed, scales, y, (int)m, (int)n, (int)k, group, nullptr, dev, st));
+  // the library's own scratch: this device's copy, looked up once (no allocation)
+  void* ws = nullptr;
+  size_t cap = 0;
+  if (w4a16::gemm_scratch(dev, &ws, &cap) != hipSuccess) return W4A16_ERR_HIP;
+  if (need > cap) return W4A16_ERR_WORKSPACE;
+  // the previous call's flags and counters may remain (a fix-up that gave up):
+  // clear them with a fill kernel (no memset node if the caller captures this)
+  const size_t off = w4a16::gemm_workspace_flags_offset(m, n, k, dev);
+  uint16_t* flags = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + off);
+  const hipError_t e = w4a16::launch_zero_fill(flags, (need - off) / 2, st);
+  if (e != hipSuccess) return W4A16_ERR_HIP;
+  return status_of(w4a16::launch_gemm(x, packed, scales, y, (int)m, (int)n, (int)k, group, ws, dev, st));
+}
+
 w4a16_status w4a16_gemm_workspace_status(void* workspace, size_t workspace_bytes, w4a16_stream_t stream) {
   if (!workspace) return W4A16_ERR_NULL;
   if (!aligned(workspace, 16)) return W4A16_ERR_ALIGN;

@@ -43,6 +43,8 @@
 //
 // For integer activations, codes and power-of-two scales every product and
 // partial sum is exact, so such inputs give bit-exact results.
+#include <mutex>
+
 #include "device.hpp"
 #include "kernels.hpp"
 #include "launch.hpp"
@@ -644,7 +646,44 @@ gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   }
 }
 
+// ---- scratch of the allocation-free entry point (w4a16_gemm_noalloc) ----
+// The split-K workspace of up to kScratchWGs persistent workgroups (256: one per
+// CU of an MI355X) lives in this file-scope device array, which every GPU the
+// library runs on holds until the process ends.  Host code never uses the
+// array's name as an address: each device's copy is looked up once, with that
+// device current, and kept in g_scratch.  Zero-initialised at load; the caller
+// clears the flags and counters before every use.
+constexpr int kScratchWGs = 256;
+constexpr size_t kScratchBytes =
+    kWorkspaceHeader + 2 * (size_t)kScratchWGs * kPartialBytes + 3 * (size_t)kScratchWGs * sizeof(uint32_t);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
 }  // namespace
+
+hipError_t gemm_scratch(const DeviceInfo& dev, void** ptr, size_t* bytes) {
+  const int d = dev.device;
+  if (d < 0 || d >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[d], [d] {
+    // dev.device is the current device (current_device_info read it)
+    void* p = nullptr;
+    g_scratch_err[d] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch[d] = g_scratch_err[d] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[d] != hipSuccess) return g_scratch_err[d];
+  *ptr = g_scratch[d];
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
+
+size_t gemm_workspace_flags_offset(int64_t m, int64_t n, int64_t k, const DeviceInfo& dev) {
+  const GemmPlan p = gemm_plan((int)m, (int)n, (int)k, dev);
+  return kWorkspaceHeader + 2 * (size_t)p.wgs * kPartialBytes;
+}
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int, const DeviceInfo& dev) {
   const GemmPlan p = gemm_plan((int)m, (int)n, (int)k, dev);

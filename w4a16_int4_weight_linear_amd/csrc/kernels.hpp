@@ -56,6 +56,11 @@ hipError_t launch_swiglu_skinny(const uint16_t* x, const uint32_t* packed, const
 // gave up waiting), padded to kWorkspaceHeader bytes; the partial tiles follow.
 constexpr size_t kWorkspaceHeader = 256;
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int group, const DeviceInfo& dev);
+// The allocation-free entry point's workspace: this device's copy of the
+// library's static scratch array (looked up once per device) and its size.
+hipError_t gemm_scratch(const DeviceInfo& dev, void** ptr, size_t* bytes);
+// Byte offset of the flags and counters (3 * workgroups uint32) in a workspace.
+size_t gemm_workspace_flags_offset(int64_t m, int64_t n, int64_t k, const DeviceInfo& dev);
 hipError_t launch_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y,
                        int m, int n, int k, int group, void* workspace, const DeviceInfo& dev,
                        hipStream_t stream);
