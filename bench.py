@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--components", default="decode,np4,batch16,swiglu,prefill,moe",
+    ap.add_argument("--components", default="decode,c1,np4,batch16,swiglu,prefill,moe,probe",
                     help="comma list of parts to measure (decode is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -144,14 +144,17 @@ def timed(torch, fn, steps, warmup, graph=False, outputs=()):
     return start.elapsed_time(stop) / steps
 
 
-def per_launch(torch, fn, steps, batches=5, graph=False, outputs=()):
-    """Mean ms per launch of fn(i): `batches` runs of `steps` back-to-back launches,
-    each run bracketed by one pair of events on the launch stream (graph=True:
-    each run is one replay of a captured graph of the `steps` launches).
-    Returns (mean, median over the runs)."""
+def per_launch(torch, fn, steps, batches=10, graph=False, outputs=()):
+    """Per-launch time of fn(i): `batches` runs of `steps` back-to-back launches, each
+    run bracketed by one pair of HIP events on the launch stream (graph=True: each
+    run is one replay of a captured graph of the `steps` launches).  Returns the mean
+    over all runs and the spread of the runs' per-launch means (ms)."""
     fn(0)
     torch.cuda.synchronize()
     g = _graph_of(torch, fn, steps) if graph else None
+    if g is not None:
+        g.replay()                       # a graph's first replay carries one-off setup
+        torch.cuda.synchronize()
     per = []
     for b in range(batches):
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -166,7 +169,19 @@ def per_launch(torch, fn, steps, batches=5, graph=False, outputs=()):
         per.append(start.elapsed_time(stop) / steps)
     if g is not None:
         _check_replay(torch, fn, steps, outputs)
-    return float(np.mean(per)), float(np.median(per))
+    p = np.array(per)
+    return {"mean": float(p.mean()), "median": float(np.median(p)), "p10": float(np.percentile(p, 10)),
+            "p90": float(np.percentile(p, 90)), "min": float(p.min()), "max": float(p.max()),
+            "runs": batches, "launches_per_run": steps}
+
+
+def timing_fields(t, work, unit_scale, unit):
+    """The per-launch record of `t` (ms) with the rate `work` / time in `unit`."""
+    rate = lambda ms: work / (ms * 1e-3) / unit_scale
+    return {"launch_ms": t["mean"], "launch_ms_median": t["median"],
+            "spread_ms": {"p10": t["p10"], "p90": t["p90"], "min": t["min"], "max": t["max"],
+                          "runs": t["runs"], "launches_per_run": t["launches_per_run"]},
+            unit: rate(t["mean"]), f"{unit}_p10_p90": [rate(t["p90"]), rate(t["p10"])]}
 
 
 def source_hash(*names):
@@ -192,6 +207,11 @@ def traffic_from_profile(kernel_file, kernel_hash):
 # ---------------------------------------------------------------------------
 # Components.
 # ---------------------------------------------------------------------------
+# Host copies of the decode workloads' inputs (x, packed, scales, group, bytes), kept
+# by the components for the oracle's one-thread timings.
+ORACLE_INPUTS = {}
+
+
 def decode_component(torch, w4, synth, args):
     up = synth.DENSE_CASES["gemv_up_1x5120x17408_g128"]
     down = synth.DENSE_CASES["gemv_down_1x17408x5120_g128"]
@@ -223,42 +243,53 @@ def decode_component(torch, w4, synth, args):
         p, s = pool_d[i % len(pool_d)]
         w4.gemv(xd_t, p, s, 128, out=yd)
 
-    up_mean, up_med = per_launch(torch, one_up, args.steps, graph=True, outputs=(yu,))
-    dn_mean, dn_med = per_launch(torch, one_down, args.steps, graph=True, outputs=(yd,))
-    launch_ms = (up_mean + dn_mean) / 2
+    t_up = per_launch(torch, one_up, args.steps, graph=True, outputs=(yu,))
+    t_dn = per_launch(torch, one_down, args.steps, graph=True, outputs=(yd,))
+    launch_ms = (t_up["mean"] + t_dn["mean"]) / 2
     launch_bytes = dense_bytes(1, up.n, up.k, 128)   # the two launches move equal bytes
     return {
         "ms_per_step": ms,
         "step_bytes": step_bytes,
         "gbs": step_bytes / (ms * 1e-3) / 1e9,
-        "kernel": {"name": "gemv_kernel<1, false>", "launch_ms_up": up_mean, "launch_ms_down": dn_mean,
-                   "launch_ms_median_up": up_med, "launch_ms_median_down": dn_med,
-                   "launch_ms": launch_ms, "bytes_per_launch": launch_bytes,
-                   "gbs": launch_bytes / (launch_ms * 1e-3) / 1e9},
+        "kernel": {"name": "gemv_kernel<1, false>", "launch_ms": launch_ms, "bytes_per_launch": launch_bytes,
+                   "gbs": launch_bytes / (launch_ms * 1e-3) / 1e9,
+                   "up": timing_fields(t_up, launch_bytes, 1e9, "gbs"),
+                   "down": timing_fields(t_dn, launch_bytes, 1e9, "gbs")},
         "inputs": (wu, xu, wd, xd),
         "quantized": ((pu, su), (pd, sd)),
     }
 
 
+def gemv_case_timing(torch, w4, synth, args, name):
+    """Per-launch timing of w4a16_gemv on one DENSE_CASES workload (graph replay, rotating pool)."""
+    c = synth.DENSE_CASES[name]
+    w, x = synth.dense_inputs(c)
+    p, s = w4.quantize(w, c.group)
+    pool = make_pool(torch, p, s)
+    xt = torch.from_numpy(x).to("cuda")
+    y = torch.empty((c.m, c.n), dtype=torch.float16, device="cuda")
+
+    def one(i):
+        pp, ss = pool[i % len(pool)]
+        w4.gemv(xt, pp, ss, c.group, out=y)
+
+    t = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+    b = dense_bytes(c.m, c.n, c.k, c.group)
+    rec = {"bytes": b, **timing_fields(t, b, 1e9, "gbs")}
+    rec["hbm_frac"] = rec["gbs"] / HBM_PEAK_GBS
+    del pool
+    ORACLE_INPUTS[name] = (x, p, s, c.group, b)    # for the one-thread oracle times
+    return rec
+
+
 def np4_component(torch, w4, synth, args):
-    out = {}
-    for name in ("gemv_np4_4x5120x5120_g128", "gemv_np4_4x5120x17408_g128"):
-        c = synth.DENSE_CASES[name]
-        w, x = synth.dense_inputs(c)
-        p, s = w4.quantize(w, c.group)
-        pool = make_pool(torch, p, s)
-        xt = torch.from_numpy(x).to("cuda")
-        y = torch.empty((c.m, c.n), dtype=torch.float16, device="cuda")
+    return {name: gemv_case_timing(torch, w4, synth, args, name)
+            for name in ("gemv_np4_4x5120x5120_g128", "gemv_np4_4x5120x17408_g128")}
 
-        def one(i):
-            pp, ss = pool[i % len(pool)]
-            w4.gemv(xt, pp, ss, c.group, out=y)
 
-        mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
-        b = dense_bytes(c.m, c.n, c.k, c.group)
-        out[name] = {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
-                     "gbs": b / (mean * 1e-3) / 1e9, "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    return out
+def c1_component(torch, w4, synth, args):
+    """The 1 x 1024 x 1024 smoke GEMV (0.54 MB: launch-latency bound, not held to the HBM bar)."""
+    return {"gemv_1x1024x1024_g128": gemv_case_timing(torch, w4, synth, args, "gemv_1x1024x1024_g128")}
 
 
 def batched_decode_component(torch, w4, synth, args):
@@ -276,10 +307,11 @@ def batched_decode_component(torch, w4, synth, args):
         pp, ss = pool[i % len(pool)]
         w4.gemm(xt, pp, ss, c.group, out=y)
 
-    mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+    t = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
     b = dense_bytes(16, c.n, c.k, c.group)
-    return {"gemm_16x5120x17408_g128": {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
-                                         "gbs": b / (mean * 1e-3) / 1e9, "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    rec = {"bytes": b, **timing_fields(t, b, 1e9, "gbs")}
+    rec["hbm_frac"] = rec["gbs"] / HBM_PEAK_GBS
+    return {"gemm_16x5120x17408_g128": rec}
 
 
 def swiglu_component(torch, w4, synth, args):
@@ -303,11 +335,11 @@ def swiglu_component(torch, w4, synth, args):
             pp, ss = pool[i % len(pool)]
             w4.gemv_swiglu(xt, pp, ss, c.group, out=y)
 
-        mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+        t = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
         b = c.n * c.k + 2 * c.n * (c.k // c.group) * 2 + m * c.k * 2 + m * c.n * 2
-        out[f"swiglu_{m}x5120x(2x17408)_g128"] = {"launch_ms": mean, "launch_ms_median": med, "bytes": b,
-                                                  "gbs": b / (mean * 1e-3) / 1e9,
-                                                  "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        rec = {"bytes": b, **timing_fields(t, b, 1e9, "gbs")}
+        rec["hbm_frac"] = rec["gbs"] / HBM_PEAK_GBS
+        out[f"swiglu_{m}x5120x(2x17408)_g128"] = rec
     return out
 
 
@@ -330,11 +362,11 @@ def prefill_component(torch, w4, synth, args):
         steps = args.steps if c.m <= 512 else max(10, args.steps // 8)
         for i in range(min(args.warmup, 10)):
             one(i)
-        mean, med = per_launch(torch, one, steps, batches=3)
+        t = per_launch(torch, one, steps, batches=5)
         fl = dense_flops(c.m, c.n, c.k)
-        out[name] = {"launch_ms": mean, "launch_ms_median": med, "flops": fl,
-                     "tflops": fl / (mean * 1e-3) / 1e12,
-                     "mfma_frac": fl / (mean * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+        rec = {"flops": fl, **timing_fields(t, fl, 1e12, "tflops")}
+        rec["mfma_frac"] = rec["tflops"] / MFMA_F16_PEAK_TFLOPS
+        out[name] = rec
     return out
 
 
@@ -356,7 +388,8 @@ def moe_component(torch, w4, synth, args):
         pp, ss = pool[i % len(pool)]
         w4.grouped_gemm(xs, pp, ss, offs, c.group, out=y)
 
-    mean, med = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+    t_moe = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+    mean = t_moe["mean"]
     b = c.experts * c.n * c.k // 2 + c.experts * c.n * (c.k // c.group) * 2 + rows * c.k * 2 + rows * c.n * 2 \
         + (c.experts + 1) * 4
     fl = dense_flops(rows, c.n, c.k)
@@ -371,7 +404,7 @@ def moe_component(torch, w4, synth, args):
         pp, ss = pool[i % len(pool)]
         w4.grouped_gemm(xs2, pp, ss, offs2, c.group, out=y)
 
-    mean2, _ = per_launch(torch, one_skewed, args.steps, graph=True, outputs=(y,))
+    mean2 = per_launch(torch, one_skewed, args.steps, graph=True, outputs=(y,))["mean"]
     # Not graded: the whole routed-expert layer on the same bank (route on the
     # device, gathered grouped product, router-weighted combine of 512 tokens).
     ids_t = torch.from_numpy(r.choice).to("cuda")
@@ -393,12 +426,12 @@ def moe_component(torch, w4, synth, args):
         pp, ss = pool[i % len(pool)]
         w4.grouped_gemm_gather(xt, tok_l, pp, ss, offs_l, c.group, out=y)
 
-    mean3, _ = per_launch(torch, layer, args.steps, graph=True, outputs=(out_l,))
-    mean4, _ = per_launch(torch, gather_only, args.steps, graph=True, outputs=(y,))
+    mean3 = per_launch(torch, layer, args.steps, graph=True, outputs=(out_l,))["mean"]
+    mean4 = per_launch(torch, gather_only, args.steps, graph=True, outputs=(y,))["mean"]
     b_gather = b - rows * c.k * 2 + c.tokens * c.k * 2 + rows * 4
     used = int(np.count_nonzero(rs.counts))
     b2 = used * (c.n * c.k // 2 + c.n * (c.k // c.group) * 2) + rows * c.k * 2 + rows * c.n * 2 + (c.experts + 1) * 4
-    return {"launch_ms": mean, "launch_ms_median": med, "bytes": b, "gbs": b / (mean * 1e-3) / 1e9,
+    return {"bytes": b, **timing_fields(t_moe, b, 1e9, "gbs"),
             "hbm_frac": b / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, "tflops": fl / (mean * 1e-3) / 1e12,
             "skewed_routing": {"experts_used": used, "max_rows": int(rs.counts.max()), "launch_ms": mean2,
                                "bytes": b2, "gbs": b2 / (mean2 * 1e-3) / 1e9},
@@ -611,15 +644,26 @@ def cpu_baseline(decode):
             break
     dt = (time.perf_counter() - t0) / reps
     dt1 = None
+    per_config = {}
     if threadpool_limits is not None:
         with threadpool_limits(1):
             t1 = time.perf_counter()
             one_step()
             dt1 = time.perf_counter() - t1
+            # each decode-shaped workload once on one thread
+            cases = dict(ORACLE_INPUTS)
+            cases["gemv_up_1x5120x17408_g128"] = (xu, pu, su, 128, decode["step_bytes"] // 2)
+            cases["gemv_down_1x17408x5120_g128"] = (xd, pd, sd, 128, decode["step_bytes"] // 2)
+            for name, (x, p, sc, g, nbytes) in sorted(cases.items()):
+                t2 = time.perf_counter()
+                oracle.linear(x, p, sc, g)
+                dt2 = time.perf_counter() - t2
+                per_config[name] = {"s": dt2, "gbs": nbytes / dt2 / 1e9}
     return {"value": decode["step_bytes"] / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{reps} decode step(s) after one warm-up (up 1x5120->17408 + down 1x17408->5120, g128): "
                       f"fp64 dequantise + numpy matmul, {dt:.2f} s per step",
             "one_thread_value": decode["step_bytes"] / dt1 / 1e9 if dt1 else None,
+            "one_thread_per_config": per_config,
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(), "blas": blas}
 
 
@@ -646,6 +690,46 @@ def environment(torch):
     return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "rocm": rocm, "torch": torch.__version__,
             "hip": torch.version.hip, "sclk_levels": sclk}
+
+
+def hbm_read_probe(torch, w4, launch_bytes, steps):
+    """The library's streaming-read probe (w4a16_hbm_read_probe): read GB/s for reads of
+    one decode launch's size, rotating over >= 1 GiB of buffers (graph replay, as the
+    GEMV is timed), and for single 1 GiB reads: the same-box denominator beside the
+    published 8 TB/s."""
+    sink = torch.empty(w4.lib.w4a16_hbm_read_probe_sink_words(), dtype=torch.int32, device="cuda")
+    size = launch_bytes // 1024 * 1024
+    bufs = [torch.empty(size // 4, dtype=torch.int32, device="cuda").random_() for _ in range(-(-POOL_BYTES // size))]
+
+    def one(i):
+        w4.hbm_read_probe(bufs[i % len(bufs)], sink)
+
+    t = per_launch(torch, one, steps, graph=True)
+    del bufs
+    big = torch.empty(POOL_BYTES // 4, dtype=torch.int32, device="cuda").random_()
+    t_big = per_launch(torch, lambda i: w4.hbm_read_probe(big, sink), 5, batches=5, graph=True)
+    del big
+    return {"launch_sized": {"bytes": size, **timing_fields(t, size, 1e9, "gbs")},
+            "one_gib": {"bytes": POOL_BYTES, **timing_fields(t_big, POOL_BYTES, 1e9, "gbs")}}
+
+
+def stamps():
+    """What was measured: a hash of the library sources (always available) and the git
+    commit (where the tree is a git checkout)."""
+    h = hashlib.sha256()
+    for d in ("w4a16_int4_weight_linear_amd/csrc", "include"):
+        for name in sorted(os.listdir(os.path.join(ROOT, d))):
+            with open(os.path.join(ROOT, d, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    commit = None
+    try:
+        import subprocess
+        r = subprocess.run(["git", "rev-parse", "HEAD"], cwd=ROOT, capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            commit = r.stdout.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return {"source_sha16": h.hexdigest()[:16], "git_commit": commit}
 
 
 def hbm_copy_reference(torch):
@@ -694,13 +778,15 @@ def main():
     res = {}
     if "decode" not in comps:
         # component runs without the headline (profiling passes): no JSON line contract
-        for name, fn in (("np4", np4_component), ("batch16", batched_decode_component),
+        for name, fn in (("c1", c1_component), ("np4", np4_component), ("batch16", batched_decode_component),
                          ("swiglu", swiglu_component), ("prefill", prefill_component), ("moe", moe_component)):
             if name in comps:
                 res[name] = fn(torch, w4, synth, args)
         print(json.dumps({"components": res}, default=float))
         return
     decode = decode_component(torch, w4, synth, args)
+    if "c1" in comps:
+        res["c1"] = c1_component(torch, w4, synth, args)
     if "np4" in comps:
         res["np4"] = np4_component(torch, w4, synth, args)
     if "batch16" in comps:
@@ -737,11 +823,26 @@ def main():
         "hbm_frac_step": round(decode["gbs"] / HBM_PEAK_GBS, 4),
     }
     line.update({key: val for key, val in res.items()})
-    if "prefill" in res and "gemm_512x5120x17408_g128" in res["prefill"]:
-        g = res["prefill"]["gemm_512x5120x17408_g128"]
-        line["gemm_m512"] = {"tflops": round(g["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                             "frac": round(g["mfma_frac"], 4), "launch_us": round(g["launch_ms"] * 1e3, 2)}
+    # the other half of the metric: the prefill GEMM against the fp16 MFMA peak
+    rooflines = {"gemv_m1": dict(line["roofline"])}
+    for name, key in (("gemm_512x5120x17408_g128", "gemm_m512"), ("gemm_4096x5120x17408_g128", "gemm_m4096")):
+        if name in res.get("prefill", {}):
+            g = res["prefill"][name]
+            rooflines[key] = {"bound": "mfma", "achieved": round(g["tflops"], 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(g["mfma_frac"], 4),
+                              "traffic": traffic_from_profile("gemm", source_hash("gemm.hip", "mfma_operands.hpp",
+                                                                                  "device.hpp")),
+                              "kernel": "gemm_kernel<128, false, true>", "launch_us": round(g["launch_ms"] * 1e3, 3),
+                              "flops_per_launch": g["flops"]}
+    line["rooflines"] = rooflines
+    if "gemm_m512" in rooflines:
+        line["gemm_m512"] = rooflines["gemm_m512"]
+    if "probe" in comps:
+        line["hbm_read_probe"] = hbm_read_probe(torch, w4, k["bytes_per_launch"], args.steps)
+        line["roofline"]["frac_of_read_probe"] = round(
+            k["gbs"] / line["hbm_read_probe"]["launch_sized"]["gbs"], 4)
     line["hbm_copy_reference"] = hbm_copy_reference(torch)
+    line["stamp"] = stamps()
     line["env"] = environment(torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(decode)

@@ -248,6 +248,25 @@ w4a16_status w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row,
                                uint16_t* out, int64_t tokens, int32_t topk, int64_t rows, int64_t n,
                                w4a16_stream_t stream);
 
+/* --------------------------------------------------------- measurement ---- */
+
+/*
+ * Streaming-read probe (measurement only, not part of the layer): reads the
+ * `bytes` bytes at `buf` (device, 16-byte aligned, bytes a multiple of 1024)
+ * once, with the decode GEMV's access pattern (one workgroup per CU, one
+ * sequential stream of 1 KiB loads per wavefront), and stores one XOR of the
+ * data per wavefront into `sink` (device uint32, at least
+ * w4a16_hbm_read_probe_sink_words() words).  Its achieved bytes/time is the
+ * same-box read bandwidth that the weight-streaming kernels are compared with,
+ * beside the published HBM peak (the infr page, Validated models & performance,
+ * gives decode GEMVs as a fraction of DRAM peak).
+ */
+w4a16_status w4a16_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                                  w4a16_stream_t stream);
+
+/* Words of `sink` w4a16_hbm_read_probe needs on the current device (0: no device). */
+int64_t w4a16_hbm_read_probe_sink_words(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,6 +126,12 @@ static void device_validation() {
   EXPECT(w4a16_moe_combine(x, off, F<const float>(), y, 4, 0, 32, 64, nullptr) == W4A16_ERR_SHAPE);
   EXPECT(w4a16_moe_combine(x, off, F<const float>(), y, INT64_MAX, 2, 32, 64, nullptr) == W4A16_ERR_SHAPE);
   EXPECT(w4a16_moe_combine(x, off, F<const float>(), y, 4, 2, 32, 64, nullptr) == W4A16_ERR_HIP);
+  EXPECT(w4a16_hbm_read_probe(fake(), 1000, F<uint32_t>(), 4096, nullptr) == W4A16_ERR_SHAPE);
+  EXPECT(w4a16_hbm_read_probe(nullptr, 1024, F<uint32_t>(), 4096, nullptr) == W4A16_ERR_NULL);
+  EXPECT(w4a16_hbm_read_probe(fake(8), 1024, F<uint32_t>(), 4096, nullptr) == W4A16_ERR_ALIGN);
+  EXPECT(w4a16_hbm_read_probe(fake(), 0, nullptr, 0, nullptr) == W4A16_OK);
+  EXPECT(w4a16_hbm_read_probe(fake(), 1024, F<uint32_t>(), 4096, nullptr) == W4A16_ERR_HIP);
+  EXPECT(w4a16_hbm_read_probe_sink_words() == 0);
 }
 
 int main() {

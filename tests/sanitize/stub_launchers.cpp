@@ -34,5 +34,9 @@ hipError_t launch_moe_route(const int32_t*, int, int, int, int32_t*, int32_t*, i
 hipError_t launch_moe_combine(const uint16_t*, const int32_t*, const float*, uint16_t*, int, int, int, int,
                               hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_zero_fill(uint16_t*, size_t, hipStream_t) { return hipErrorNoDevice; }
+int probe_sink_words(const DeviceInfo& dev) { return dev.num_cu * 8; }
+hipError_t launch_stream_read(const void*, size_t, uint32_t*, const DeviceInfo&, hipStream_t) {
+  return hipErrorNoDevice;
+}
 
 }  // namespace w4a16

@@ -50,6 +50,8 @@ SIGNATURES = {
     "w4a16_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "w4a16_gemm_workspace_status": (ctypes.c_int, [_vp, _sz, _vp]),
     "w4a16_gemm_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
+    "w4a16_hbm_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _sz, _vp]),
+    "w4a16_hbm_read_probe_sink_words": (_i64, []),
     "w4a16_grouped_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_gemv_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "w4a16_moe_route": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -264,6 +266,14 @@ def gemm_noalloc(x, packed, scales, group: int, out=None, stream=None):
     return out
 
 
+def hbm_read_probe(buf, sink, stream=None):
+    """Read all of `buf` (a device tensor, 1 KiB multiple) once; one XOR per wave goes to
+    `sink` (int32, at least lib.w4a16_hbm_read_probe_sink_words() elements)."""
+    _check_tensors("hbm_read_probe", [("sink", sink, "i32", None)])
+    _check(lib.w4a16_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), sink.numel(),
+                                    _stream(stream)), "w4a16_hbm_read_probe")
+
+
 def gemm_workspace_status(workspace, stream=None) -> int:
     """Status word of a gemm workspace (host-synchronous diagnostic): OK, or ERR_TIMEOUT if a
     split-K fix-up of an earlier call gave up waiting (its tiles were written as NaN)."""
@@ -364,5 +374,6 @@ def moe_combine(y_pairs, pair_row, weights, out=None, stream=None):
 
 
 __all__ = ["lib", "LIB_PATH", "SIGNATURES", "W4A16Error", "quantize", "pack", "unpack", "gemv", "gemm",
-           "gemm_workspace", "gemm_workspace_status", "gemm_noalloc", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
+           "gemm_workspace", "gemm_workspace_status", "gemm_noalloc",
+           "hbm_read_probe", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
            "grouped_gemm_gather", "moe_combine"] + list(SIGNATURES)

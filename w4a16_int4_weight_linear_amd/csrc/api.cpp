@@ -364,4 +364,24 @@ w4a16_status w4a16_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row,
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
+int64_t w4a16_hbm_read_probe_sink_words(void) {
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return 0;
+  return w4a16::probe_sink_words(dev);
+}
+
+w4a16_status w4a16_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                                  w4a16_stream_t stream) {
+  if (bytes % 1024) return W4A16_ERR_SHAPE;
+  if (bytes == 0) return W4A16_OK;
+  if (!buf || !sink) return W4A16_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return W4A16_ERR_ALIGN;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  if (sink_words < (size_t)w4a16::probe_sink_words(dev)) return W4A16_ERR_SHAPE;
+  // each wave addresses its own range with 32-bit offsets
+  if (bytes / (size_t)w4a16::probe_sink_words(dev) >= (size_t)1 << 30) return W4A16_ERR_SHAPE;
+  return status_of(w4a16::launch_stream_read(buf, bytes, sink, dev, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

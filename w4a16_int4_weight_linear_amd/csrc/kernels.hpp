@@ -83,6 +83,11 @@ hipError_t launch_moe_route(const int32_t* ids, int pairs, int topk, int experts
 hipError_t launch_moe_combine(const uint16_t* y_pairs, const int32_t* pair_row, const float* weights, uint16_t* out,
                               int tokens, int topk, int n, int rows, hipStream_t stream);
 
+// ---- streaming-read HBM probe (probe.hip) ----
+int probe_sink_words(const DeviceInfo& dev);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, const DeviceInfo& dev,
+                              hipStream_t stream);
+
 // ---- y = 0 (the empty sum, k == 0) ----
 hipError_t launch_zero_fill(uint16_t* y, size_t count, hipStream_t stream);
 
