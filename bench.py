@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--components", default="decode,c1,np4,batch16,swiglu,prefill,moe,probe",
+    ap.add_argument("--components", default="decode,c1,np4,batch16,swiglu,prefill,moe,moe_ffn,probe",
                     help="comma list of parts to measure (decode is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -439,6 +439,66 @@ def moe_component(torch, w4, synth, args):
             "layer_route_gather_combine": {"ms": mean3, "tokens": c.tokens}}
 
 
+def moe_ffn_component(torch, w4, synth, args):
+    """The routed experts' whole FFN at the 35B-A3B-like shape (256 experts, hidden 2048,
+    intermediate 512, g32, 512 tokens top-8): route, gathered gate/up + SwiGLU, down
+    projection, combine, one step timed by graph replay, plus the two grouped products
+    alone.  GB/s over each part's algorithmic bytes (weights of the experts that receive
+    rows - all 256 here - plus the activations each step reads and writes once)."""
+    c = synth.FFN_CASES["moe_ffn_256e_h2048_i512_g32_top8"]
+    gu_q, gu_s, dn_q, dn_s, x, r, wts = synth.moe_ffn_inputs(c)
+    gu = np.stack([w4.pack(gu_q[e]) for e in range(c.experts)])
+    dn = np.stack([w4.pack(dn_q[e]) for e in range(c.experts)])
+    del gu_q, dn_q
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int32) if a.dtype == np.uint32 else
+                                   np.ascontiguousarray(a)).to("cuda")
+    bank = (t(gu), t(gu_s), t(dn), t(dn_s))
+    per = sum(b.numel() * b.element_size() for b in bank)
+    pool = [bank] + [tuple(b.clone() for b in bank) for _ in range(max(1, -(-POOL_BYTES // per) - 1))]
+    rows = c.tokens * c.topk
+    ids, xt, wt = t(r.choice.astype(np.int32)), t(x), t(wts)
+    offs = torch.empty(c.experts + 1, dtype=torch.int32, device="cuda")
+    tok = torch.empty(rows, dtype=torch.int32, device="cuda")
+    row = torch.empty((c.tokens, c.topk), dtype=torch.int32, device="cuda")
+    h = torch.empty((rows, c.inter), dtype=torch.float16, device="cuda")
+    yp = torch.empty((rows, c.hidden), dtype=torch.float16, device="cuda")
+    out = torch.empty((c.tokens, c.hidden), dtype=torch.float16, device="cuda")
+    st = lambda: w4._stream(None)
+
+    def route():
+        w4._check(w4.lib.w4a16_moe_route(w4._ptr(ids), c.tokens, c.topk, c.experts, w4._ptr(offs), w4._ptr(tok),
+                                         w4._ptr(row), st()), "w4a16_moe_route")
+
+    def gate_up(i):
+        g, gs, _, _ = pool[i % len(pool)]
+        w4.grouped_gemm_swiglu(xt, g, gs, offs, c.group, pair_token=tok, out=h)
+
+    def down(i):
+        _, _, d, ds = pool[i % len(pool)]
+        w4.grouped_gemm(h, d, ds, offs, c.group, out=yp)
+
+    def step(i):
+        route()
+        gate_up(i)
+        down(i)
+        w4.moe_combine(yp, row, wt, out=out)
+
+    t_step = per_launch(torch, step, args.steps, graph=True, outputs=(out,))
+    route()
+    t_gu = per_launch(torch, gate_up, args.steps, graph=True, outputs=(h,))
+    t_dn = per_launch(torch, down, args.steps, graph=True, outputs=(yp,))
+    gu_w = bank[0].numel() * 4 + bank[1].numel() * 2
+    dn_w = bank[2].numel() * 4 + bank[3].numel() * 2
+    b_gu = gu_w + c.tokens * c.hidden * 2 + rows * 4 + rows * c.inter * 2 + (c.experts + 1) * 4
+    b_dn = dn_w + rows * c.inter * 2 + rows * c.hidden * 2 + (c.experts + 1) * 4
+    b_step = (b_gu + b_dn + rows * c.hidden * 2 + c.tokens * c.hidden * 2 + rows * 8 + rows * 4  # combine
+              + rows * 4 * 3 + (c.experts + 1) * 4)                                              # routing
+    fl = 2 * rows * (2 * c.inter) * c.hidden + 2 * rows * c.hidden * c.inter
+    return {"workload": c.name, "step": {"bytes": b_step, "flops": fl, **timing_fields(t_step, b_step, 1e9, "gbs")},
+            "gate_up_swiglu": {"bytes": b_gu, **timing_fields(t_gu, b_gu, 1e9, "gbs")},
+            "down": {"bytes": b_dn, **timing_fields(t_dn, b_dn, 1e9, "gbs")}}
+
+
 def traffic_probe(torch, w4, synth):
     """Launch sequence for the HBM counter passes: three plain elementwise copies
     of a 256 MiB fp16 buffer (known traffic: 256 MiB read + 256 MiB written each),
@@ -779,7 +839,8 @@ def main():
     if "decode" not in comps:
         # component runs without the headline (profiling passes): no JSON line contract
         for name, fn in (("c1", c1_component), ("np4", np4_component), ("batch16", batched_decode_component),
-                         ("swiglu", swiglu_component), ("prefill", prefill_component), ("moe", moe_component)):
+                         ("swiglu", swiglu_component), ("prefill", prefill_component), ("moe", moe_component),
+                         ("moe_ffn", moe_ffn_component)):
             if name in comps:
                 res[name] = fn(torch, w4, synth, args)
         print(json.dumps({"components": res}, default=float))
@@ -797,6 +858,8 @@ def main():
         res["prefill"] = prefill_component(torch, w4, synth, args)
     if "moe" in comps:
         res["moe"] = moe_component(torch, w4, synth, args)
+    if "moe_ffn" in comps:
+        res["moe_ffn"] = moe_ffn_component(torch, w4, synth, args)
 
     k = decode["kernel"]
     traffic = traffic_from_profile("gemv", source_hash("gemv.hip", "device.hpp"))

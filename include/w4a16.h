@@ -239,6 +239,24 @@ w4a16_status w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_to
                                        int64_t k, int32_t group, w4a16_stream_t stream);
 
 /*
+ * The experts' fused gate/up projection with its SwiGLU activation (the
+ * expert_gateup role of the infr page's benchmarking section; the SwiGLU of the
+ * rust-inference page; gate and up fused as the infr page's Linear + GatedAct):
+ * packed [E, 2n, k/8] and scales [E, 2n, k/group] interleave each expert's gate
+ * (even) and up (odd) weight rows; y [rows, n] row r = fp16(SiLU(g) * u) with
+ * g, u the fp32-accumulated products of row r's activations with its expert's
+ * gate and up rows, SiLU(g) = g / (1 + e^-g) in fp32.  With pair_token NULL, x
+ * [rows, k] holds the rows sorted by expert (as for w4a16_grouped_gemm; tokens
+ * is ignored); otherwise x [tokens, k] holds the token rows and grouped row r
+ * reads x[pair_token[r]] (as for w4a16_grouped_gemm_gather).  offsets as for
+ * w4a16_grouped_gemm.  The 2 x rows x n intermediate never leaves the chip.
+ */
+w4a16_status w4a16_grouped_gemm_swiglu(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
+                                       const uint16_t* scales, const int32_t* offsets, uint16_t* y,
+                                       int32_t num_experts, int64_t rows, int64_t tokens, int64_t n, int64_t k,
+                                       int32_t group, w4a16_stream_t stream);
+
+/*
  * Router-weighted combine: out [tokens, n] fp16, out[t] = sum over slots j (in
  * order) of weights[t, j] * y_pairs[pair_row[t, j]], accumulated in fp32 and
  * rounded once.  y_pairs [rows, n] fp16 (the grouped product), weights fp32

@@ -14,10 +14,11 @@ loops).  No function here is left "parity unpinned".
 
 from .reference import (GROUPS, quantize, pack, unpack, dequantize, linear, linear_rows,
                         linear_cols, linear_loops, grouped_linear, silu, swiglu_linear, moe_route,
-                        moe_combine, moe_layer)
+                        moe_combine, moe_layer, grouped_swiglu_linear, moe_ffn)
 from .check import compare, Report, ELEM_TOL, ROW_TOL
 
 __all__ = ["GROUPS", "quantize", "pack", "unpack", "dequantize", "linear", "linear_rows",
            "linear_cols", "linear_loops", "grouped_linear", "silu", "swiglu_linear", "moe_route", "moe_combine", "moe_layer",
+           "grouped_swiglu_linear", "moe_ffn",
            "compare", "Report",
            "ELEM_TOL", "ROW_TOL"]

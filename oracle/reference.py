@@ -249,3 +249,43 @@ def moe_layer(x: np.ndarray, topk_ids: np.ndarray, weights: np.ndarray, packed: 
         for r in range(len(ts)):
             out[ts[r]] += w[ts[r], js[r]] * ye[r]
     return out
+
+
+# ---------------------------------------------------------------------------
+# The routed experts' feed-forward: each expert's fused gate/up projection with
+# its SwiGLU activation, then its down projection, combined with the router
+# weights (the expert_gateup / expert_down roles of the infr page's
+# benchmarking section; SwiGLU as on the rust-inference page).  Reading: the
+# SwiGLU output is the down projection's input activation, and activations are
+# fp16 in the W4A16 scheme, so it is rounded to fp16 (nearest even) in between;
+# everything else is fp64.
+# ---------------------------------------------------------------------------
+def grouped_swiglu_linear(x_sorted: np.ndarray, packed: np.ndarray, s: np.ndarray,
+                          offsets: np.ndarray, group: int) -> np.ndarray:
+    """Rows offsets[e]..offsets[e+1]-1 of x_sorted through expert e's interleaved gate/up
+    rows: y[r] = SiLU(x[r] . Wg_e^T) * (x[r] . Wu_e^T), fp64 (packed [E, 2N, K/8])."""
+    x_sorted = np.asarray(x_sorted, dtype=np.float16)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    out = np.zeros((x_sorted.shape[0], packed.shape[1] // 2), dtype=np.float64)
+    for e in range(packed.shape[0]):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            out[r0:r1] = swiglu_linear(x_sorted[r0:r1], packed[e], s[e], group)
+    return out
+
+
+def moe_ffn(x: np.ndarray, topk_ids: np.ndarray, weights: np.ndarray, gu_packed: np.ndarray, gu_s: np.ndarray,
+            dn_packed: np.ndarray, dn_s: np.ndarray, group: int) -> np.ndarray:
+    """out[t] = sum_j w[t, j] * (h[t, j] . Wd_e^T), e = topk_ids[t, j], with
+    h[t, j] = fp16(SiLU(x[t] . Wg_e^T) * (x[t] . Wu_e^T)); fp64 otherwise."""
+    x = np.asarray(x, dtype=np.float16)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.float64)
+    out = np.zeros((x.shape[0], dn_packed.shape[1]), dtype=np.float64)
+    for e in np.unique(ids):
+        ts, js = np.nonzero(ids == e)
+        h = swiglu_linear(x[ts], gu_packed[e], gu_s[e], group).astype(np.float16)
+        yd = linear(h, dn_packed[e], dn_s[e], group)
+        for r in range(len(ts)):
+            out[ts[r]] += w[ts[r], js[r]] * yd[r]
+    return out

@@ -78,6 +78,25 @@ MOE_CASES = {
 }
 
 
+@dataclass
+class MoEFFNCase:
+    name: str
+    seed: int
+    tokens: int
+    experts: int
+    topk: int
+    hidden: int        # the layer's input and output width (gate/up K, down N)
+    inter: int         # the expert's intermediate width (gate/up outputs, down K)
+    group: int
+
+
+# The routed experts' whole feed-forward at the 35B-A3B-like shape: per expert a
+# fused gate/up projection [2 x 512, 2048] and a down projection [2048, 512], g32.
+FFN_CASES = {
+    "moe_ffn_256e_h2048_i512_g32_top8": MoEFFNCase("moe_ffn_256e_h2048_i512_g32_top8", 8, 512, 256, 8, 2048, 512, 32),
+}
+
+
 def dense_inputs(case: DenseCase, max_x_rows: int | None = None):
     """Draw (w fp32 [n, k], x fp16 [m, k]) for a dense case.
 
@@ -174,3 +193,32 @@ def power_of_two_scales(rng: np.random.Generator, n: int, groups: int, lo: int =
     """fp16 scales 2^e with e uniform in [lo, hi] (exact-arithmetic family)."""
     e = rng.integers(lo, hi + 1, size=(n, groups))
     return np.ldexp(np.ones((n, groups)), e).astype(np.float16)
+
+
+def code_bank(rng: np.random.Generator, experts: int, n: int, k: int) -> np.ndarray:
+    """int8 weight codes [experts, n, k] uniform in [-7, 7]: the range a symmetric int4
+    quantiser gives Gaussian weights (its -8 is never reached)."""
+    return rng.integers(-7, 8, size=(experts, n, k), dtype=np.int8)
+
+
+def scale_bank(rng: np.random.Generator, experts: int, n: int, groups: int) -> np.ndarray:
+    """fp16 group scales [experts, n, groups] of the size a group of 32 N(0, 0.02^2)
+    weights gets: 0.02 * U(1.5, 3.0) / 7, rounded to fp16."""
+    return (WEIGHT_STD * rng.uniform(1.5, 3.0, size=(experts, n, groups)) / 7).astype(np.float16)
+
+
+def moe_ffn_inputs(case: MoEFFNCase):
+    """The routed-expert FFN drawn directly in quantised form (codes and scales), so both
+    sides pack the same codes with their own code (quantising the 805 M Gaussian weights
+    of the full bank on the host would take minutes).  Returns (gate/up codes [E, 2I, H]
+    with gate rows even and up rows odd, their scales, down codes [E, H, I], their scales,
+    x fp16 [T, H], routing, router weights fp32 [T, topk])."""
+    rng = np.random.default_rng(case.seed)
+    gu_q = code_bank(rng, case.experts, 2 * case.inter, case.hidden)
+    gu_s = scale_bank(rng, case.experts, 2 * case.inter, case.hidden // case.group)
+    dn_q = code_bank(rng, case.experts, case.hidden, case.inter)
+    dn_s = scale_bank(rng, case.experts, case.hidden, case.inter // case.group)
+    x = activations(rng, case.tokens, case.hidden)
+    routing = route_uniform(rng, case.tokens, case.experts, case.topk)
+    w = router_weights(rng, case.tokens, case.topk)
+    return gu_q, gu_s, dn_q, dn_s, x, routing, w

@@ -119,6 +119,13 @@ static void device_validation() {
   const int32_t* tok = F<const int32_t>();
   EXPECT(w4a16_grouped_gemm_gather(x, nullptr, p, s, off, y, 4, 16, 8, 64, 128, 32, nullptr) == W4A16_ERR_NULL);
   EXPECT(w4a16_grouped_gemm_gather(x, tok, p, s, off, y, 4, 16, 8, 64, 128, 32, nullptr) == W4A16_ERR_HIP);
+  EXPECT(w4a16_grouped_gemm_swiglu(x, nullptr, p, s, off, y, 4, 16, 0, 64, 128, 48, nullptr) == W4A16_ERR_GROUP);
+  EXPECT(w4a16_grouped_gemm_swiglu(x, nullptr, p, s, off, y, 4, 16, 0, (int64_t)1 << 30, 128, 32, nullptr) ==
+         W4A16_ERR_SHAPE);
+  EXPECT(w4a16_grouped_gemm_swiglu(x, F<const int32_t>(2), p, s, off, y, 4, 16, 8, 64, 128, 32, nullptr) ==
+         W4A16_ERR_ALIGN);
+  EXPECT(w4a16_grouped_gemm_swiglu(x, nullptr, p, s, off, y, 4, 16, 0, 64, 128, 32, nullptr) == W4A16_ERR_HIP);
+  EXPECT(w4a16_grouped_gemm_swiglu(x, tok, p, s, off, y, 4, 16, 8, 64, 128, 32, nullptr) == W4A16_ERR_HIP);
   int32_t* o = F<int32_t>();
   EXPECT(w4a16_moe_route(off, 4, 0, 8, o, o, o, nullptr) == W4A16_ERR_SHAPE);
   EXPECT(w4a16_moe_route(off, INT64_MAX, 8, 8, o, o, o, nullptr) == W4A16_ERR_SHAPE);

@@ -28,6 +28,9 @@ hipError_t launch_grouped_gemm(const uint16_t*, const uint32_t*, const uint16_t*
 hipError_t launch_grouped_gemm_gather(const uint16_t*, const int32_t*, int, const uint32_t*, const uint16_t*,
                                       const int32_t*, uint16_t*, int, int, int, int, int, const DeviceInfo&,
                                       hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_grouped_gemm_swiglu(const uint16_t*, const int32_t*, int, const uint32_t*, const uint16_t*,
+                                      const int32_t*, uint16_t*, int, int, int, int, int, const DeviceInfo&,
+                                      hipStream_t) { return hipErrorNoDevice; }
 size_t moe_route_lds(int experts) { return (size_t)experts * 4; }
 hipError_t launch_moe_route(const int32_t*, int, int, int, int32_t*, int32_t*, int32_t*, const DeviceInfo&,
                             hipStream_t) { return hipErrorNoDevice; }

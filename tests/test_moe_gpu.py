@@ -118,3 +118,90 @@ def test_moe_layer_full_size(w4):
     torch.cuda.synchronize()
     rep = assert_close(out, oracle.moe_layer(x, r.choice, wts, p_ref, s_ref, case.group), "MoE layer")
     print(f"MoE layer: {rep.message}")
+
+
+# ---------------------------------------------------------------------------
+# The experts' whole feed-forward: fused gate/up + SwiGLU, down projection, combine.
+# ---------------------------------------------------------------------------
+def _packed_banks(w4, q):
+    """(library-packed, oracle-packed) words of an int8 code bank [E, n, k]."""
+    lib = np.stack([w4.pack(q[e]) for e in range(q.shape[0])])
+    ref = np.stack([oracle.pack(q[e]) for e in range(q.shape[0])])
+    return lib, ref
+
+
+@pytest.mark.parametrize("experts,n,k,group,counts", [
+    (4, 96, 256, 32, [3, 0, 21, 40]),
+    (3, 100, 384, 128, [1, 33, 7]),          # n even but not a multiple of 4: scalar stores
+    (5, 512, 2048, 32, [16, 5, 0, 29, 64]),  # the expert gate/up shape (2 x 512 rows, K = 2048)
+])
+def test_grouped_swiglu_sorted_and_gathered(w4, experts, n, k, group, counts):
+    rng = np.random.default_rng(7600 + n + k)
+    q = synth.code_bank(rng, experts, 2 * n, k)
+    s = synth.scale_bank(rng, experts, 2 * n, k // group)
+    p, p_ref = _packed_banks(w4, q)
+    rows = int(sum(counts))
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    tokens = 50
+    x = synth.activations(rng, tokens, k)
+    tok = rng.integers(0, tokens, size=rows).astype(np.int32)
+    y_ref = oracle.grouped_swiglu_linear(x[tok], p_ref, s, offs, group)
+    y1 = host(w4.grouped_gemm_swiglu(dev(x[tok]), dev(p), dev(s), dev(offs), group))
+    assert_close(y1, y_ref, f"sorted E={experts} n={n} k={k}")
+    y2 = host(w4.grouped_gemm_swiglu(dev(x), dev(p), dev(s), dev(offs), group, pair_token=dev(tok)))
+    assert_close(y2, y_ref, f"gathered E={experts} n={n} k={k}")
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+def test_grouped_swiglu_gate_roles(w4):
+    """Zero gate scales give exact zeros (SiLU(0) = 0) whatever the up rows hold; zero
+    up scales likewise: the even rows are the gate, the odd rows the up projection."""
+    rng = np.random.default_rng(7700)
+    experts, n, k, counts = 3, 64, 256, [5, 17, 2]
+    q = synth.code_bank(rng, experts, 2 * n, k)
+    s = synth.scale_bank(rng, experts, 2 * n, k // 32)
+    p, _ = _packed_banks(w4, q)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synth.activations(rng, int(sum(counts)), k)
+    for zero_rows in (0, 1):
+        s0 = s.copy()
+        s0[:, zero_rows::2] = 0
+        y = host(w4.grouped_gemm_swiglu(dev(x), dev(p), dev(s0), dev(offs), 32))
+        assert not np.any(y.view(np.uint16) & 0x7FFF), f"rows {zero_rows}::2 zeroed"
+
+
+def test_expert_down_projection_full_size(w4):
+    """The experts' down projection (K = 512 -> N = 2048, g32) at the full 256-expert,
+    4096-pair shape, bit-exact on the integer family."""
+    rng = np.random.default_rng(7800)
+    r = synth.route_uniform(rng, 512, 256, 8)
+    q = rng.integers(-8, 8, size=(256, 2048, 512), dtype=np.int8)
+    s = synth.power_of_two_scales(rng, 256 * 2048, 512 // 32, lo=-6, hi=-3).reshape(256, 2048, 16)
+    p, p_ref = _packed_banks(w4, q)
+    xs = synth.integer_activations(rng, len(r.pair_token), 512)
+    y = host(w4.grouped_gemm(dev(xs), dev(p), dev(s), dev(r.offsets), 32))
+    assert_bit_exact(y, oracle.grouped_linear(xs, p_ref, s, r.offsets, 32), "expert down 256 x [2048, 512]")
+
+
+def run_moe_ffn(w4, x, ids, wts, gu, gus, dn, dns, experts, group, inter):
+    """route -> gathered gate/up + SwiGLU -> down -> combine, all on the device."""
+    offs, tok, row = w4.moe_route(ids, experts)
+    h = w4.grouped_gemm_swiglu(x, gu, gus, offs, group, pair_token=tok)
+    yp = w4.grouped_gemm(h, dn, dns, offs, group)
+    return w4.moe_combine(yp, row, wts)
+
+
+def test_moe_ffn_full_size(w4):
+    """The routed experts' whole FFN at the 35B-A3B-like shape (256 experts, hidden 2048,
+    intermediate 512, top-8 of 512 tokens, g32) against the oracle's moe_ffn, every output."""
+    case = synth.FFN_CASES["moe_ffn_256e_h2048_i512_g32_top8"]
+    gu_q, gu_s, dn_q, dn_s, x, r, wts = synth.moe_ffn_inputs(case)
+    gu, gu_ref = _packed_banks(w4, gu_q)
+    dn, dn_ref = _packed_banks(w4, dn_q)
+    del gu_q, dn_q
+    out = run_moe_ffn(w4, dev(x), dev(r.choice.astype(np.int32)), dev(wts), dev(gu), dev(gu_s), dev(dn), dev(dn_s),
+                      case.experts, case.group, case.inter)
+    y = host(out)
+    ref = oracle.moe_ffn(x, r.choice, wts, gu_ref, gu_s, dn_ref, dn_s, case.group)
+    rep = assert_close(y, ref, "moe ffn full size")
+    print(f"moe ffn: {rep.message}")

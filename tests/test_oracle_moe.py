@@ -88,3 +88,75 @@ def test_combine_hand_example():
     # token 0: 0.5 * row 2 + 0.25 * row 1 = (1.5 + 0.5, 15 + 5)
     # token 1: 2 * row 0 - 1 * row 3 = (2 - 4, 20 - 40)
     assert out.tolist() == [[2.0, 20.0], [-2.0, -20.0]]
+
+
+def _unit_bank(codes_per_row, k, group, scale):
+    """One expert whose weight rows have the given {position: code} maps, all scales `scale`."""
+    q = np.zeros((len(codes_per_row), k), np.int8)
+    for r, m in enumerate(codes_per_row):
+        for pos, c in m.items():
+            q[r, pos] = c
+    s = np.full((len(codes_per_row), k // group), scale, np.float16)
+    return oracle.pack(q)[None], s[None]
+
+
+def test_moe_ffn_hand_example():
+    """One token routed to one expert with router weight 1/2, values worked out by hand.
+
+    x = 32 ones.  Gate/up rows interleave (row 2i gate, 2i + 1 up), scale 1:
+    pair 0: gate = 8 codes of 5 -> g = 40, SiLU(40) = 40 in fp64; up = one 3 -> u = 3; h0 = 120
+    pair 1: gate = 40 again, up = one -1 -> h1 = -40; pairs 2..31 all zero -> h = 0.
+    Down (k = 32 = the 32 pairs): row 0 codes 1 at 0, 2 at 1, scale 1/2 -> (120 - 80) / 2 = 20;
+    row 1 code -1 at 0, scale 1/4 -> -30.  out = 1/2 * (20, -30) = (10, -15).
+    """
+    gate40 = {p: 5 for p in range(8)}
+    rows = [gate40, {3: 3}, gate40, {7: -1}] + [{}] * 60
+    gu_p, gu_s = _unit_bank(rows, 32, 32, 1.0)
+    dn_p0, dn_s0 = _unit_bank([{0: 1, 1: 2}], 32, 32, 0.5)
+    dn_p1, dn_s1 = _unit_bank([{0: -1}], 32, 32, 0.25)
+    dn_p, dn_s = np.concatenate([dn_p0, dn_p1], axis=1), np.concatenate([dn_s0, dn_s1], axis=1)
+    x = np.ones((1, 32), np.float16)
+    out = oracle.moe_ffn(x, np.array([[0]]), np.array([[0.5]], np.float32), gu_p, gu_s, dn_p, dn_s, 32)
+    assert out.tolist() == [[10.0, -15.0]]
+    # gate and up swapped in the bank: SiLU(3) * 40 is not an integer, so the example would fail
+    swapped = [rows[1], rows[0], rows[3], rows[2]] + rows[4:]
+    gu_q, _ = _unit_bank(swapped, 32, 32, 1.0)
+    assert oracle.moe_ffn(x, np.array([[0]]), np.array([[0.5]], np.float32), gu_q, gu_s, dn_p, dn_s,
+                          32).tolist() != [[10.0, -15.0]]
+
+
+def test_grouped_swiglu_is_silu_of_gate_times_up():
+    """The grouped SwiGLU product equals SiLU of the grouped product over the gate (even)
+    rows times the grouped product over the up (odd) rows, expert by expert."""
+    rng = np.random.default_rng(8)
+    experts, n, k = 5, 24, 64
+    q = np.stack([synth.integer_codes(rng, 2 * n, k) for _ in range(experts)])
+    s = np.stack([synth.power_of_two_scales(rng, 2 * n, k // 32, lo=-6, hi=-3) for _ in range(experts)])
+    packed = np.stack([oracle.pack(q[e]) for e in range(experts)])
+    counts = [3, 0, 7, 1, 4]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    xs = synth.integer_activations(rng, int(sum(counts)), k)
+    gate = oracle.grouped_linear(xs, packed[:, 0::2], s[:, 0::2], offsets, 32)
+    up = oracle.grouped_linear(xs, packed[:, 1::2], s[:, 1::2], offsets, 32)
+    got = oracle.grouped_swiglu_linear(xs, packed, s, offsets, 32)
+    assert np.allclose(got, oracle.silu(gate) * up, rtol=1e-15, atol=0)
+
+
+def test_moe_ffn_reduces_to_its_steps():
+    """route -> grouped SwiGLU -> fp16 -> grouped down -> combine is the FFN."""
+    rng = np.random.default_rng(9)
+    experts, t_count, topk, hid, inter = 6, 11, 2, 64, 32
+    gq = np.stack([synth.integer_codes(rng, 2 * inter, hid) for _ in range(experts)])
+    gs = np.stack([synth.power_of_two_scales(rng, 2 * inter, hid // 32, lo=-8, hi=-5) for _ in range(experts)])
+    dq = np.stack([synth.integer_codes(rng, hid, inter) for _ in range(experts)])
+    ds = np.stack([synth.power_of_two_scales(rng, hid, inter // 32, lo=-6, hi=-3) for _ in range(experts)])
+    gp = np.stack([oracle.pack(a) for a in gq])
+    dp = np.stack([oracle.pack(a) for a in dq])
+    x = synth.integer_activations(rng, t_count, hid)
+    ids = np.stack([rng.choice(experts, topk, replace=False) for _ in range(t_count)])
+    w = synth.router_weights(rng, t_count, topk)
+    offsets, tok, slot, row = oracle.moe_route(ids, experts)
+    h = oracle.grouped_swiglu_linear(x[tok], gp, gs, offsets, 32).astype(np.float16)
+    yp = oracle.grouped_linear(h, dp, ds, offsets, 32)
+    want = oracle.moe_combine(yp, row, w)
+    assert np.allclose(oracle.moe_ffn(x, ids, w, gp, gs, dp, ds, 32), want, rtol=1e-13, atol=1e-13)

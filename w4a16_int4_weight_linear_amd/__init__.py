@@ -58,6 +58,8 @@ SIGNATURES = {
     "w4a16_grouped_gemm_gather": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i32,
                                                  _vp]),
     "w4a16_moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp]),
+    "w4a16_grouped_gemm_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i32,
+                                                 _vp]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():
@@ -359,6 +361,32 @@ def grouped_gemm_gather(x, pair_token, packed, scales, offsets, group: int, out=
     return out
 
 
+def grouped_gemm_swiglu(x, packed, scales, offsets, group: int, pair_token=None, out=None, stream=None):
+    """Experts' fused gate/up + SwiGLU: packed [E, 2n, k/8] interleaves gate/up rows; y [rows, n].
+    pair_token None: x [rows, k] is sorted by expert; else grouped row r reads x[pair_token[r]]."""
+    _require_tensors("grouped_gemm_swiglu", x=x)
+    if x.dim() != 2:
+        raise ValueError("grouped_gemm_swiglu: x must be 2-D")
+    x_rows, k = x.shape
+    experts, n2, bank = _bank_shapes("grouped_gemm_swiglu", packed, scales, k, group)
+    if n2 % 2:
+        raise ValueError("grouped_gemm_swiglu: packed must have a multiple of 2 rows per expert")
+    specs = [("x", x, "f16", None)] + bank + [("offsets", offsets, "i32", (experts + 1,))]
+    if pair_token is not None:
+        _require_tensors("grouped_gemm_swiglu", pair_token=pair_token)
+        if pair_token.dim() != 1:
+            raise ValueError("grouped_gemm_swiglu: pair_token must be [rows]")
+        specs.append(("pair_token", pair_token, "i32", None))
+        rows = pair_token.shape[0]
+    else:
+        rows = x_rows
+    out = _checked_out("grouped_gemm_swiglu", specs, out, (rows, n2 // 2), x)
+    _check(lib.w4a16_grouped_gemm_swiglu(_ptr(x), _ptr(pair_token), _ptr(packed), _ptr(scales), _ptr(offsets),
+                                         _ptr(out), experts, rows, x_rows, n2 // 2, k, group, _stream(stream)),
+           "w4a16_grouped_gemm_swiglu")
+    return out
+
+
 def moe_combine(y_pairs, pair_row, weights, out=None, stream=None):
     """out [tokens, n] = sum_j weights[t, j] * y_pairs[pair_row[t, j]] (weights fp32 [tokens, topk])."""
     _require_tensors("moe_combine", y_pairs=y_pairs, pair_row=pair_row, weights=weights)
@@ -375,5 +403,5 @@ def moe_combine(y_pairs, pair_row, weights, out=None, stream=None):
 
 __all__ = ["lib", "LIB_PATH", "SIGNATURES", "W4A16Error", "quantize", "pack", "unpack", "gemv", "gemm",
            "gemm_workspace", "gemm_workspace_status", "gemm_noalloc",
-           "hbm_read_probe", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
+           "hbm_read_probe", "grouped_gemm_swiglu", "grouped_gemm", "interleave_rows", "gemv_swiglu", "moe_route",
            "grouped_gemm_gather", "moe_combine"] + list(SIGNATURES)

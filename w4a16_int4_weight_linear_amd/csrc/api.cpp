@@ -333,6 +333,32 @@ w4a16_status w4a16_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_to
                                                      num_experts, (int)rows, (int)n, (int)k, group, dev, st));
 }
 
+w4a16_status w4a16_grouped_gemm_swiglu(const uint16_t* x, const int32_t* pair_token, const uint32_t* packed,
+                                       const uint16_t* scales, const int32_t* offsets, uint16_t* y,
+                                       int32_t num_experts, int64_t rows, int64_t tokens, int64_t n, int64_t k,
+                                       int32_t group, w4a16_stream_t stream) {
+  if (!valid_group(group)) return W4A16_ERR_GROUP;
+  if (num_experts < 0 || rows < 0 || tokens < 0 || n < 0 || k < 0 || k % group) return W4A16_ERR_SHAPE;
+  if (rows > kMaxDim || tokens > kMaxDim || n > kMaxDim / 2 || k > kMaxDim) return W4A16_ERR_SHAPE;
+  if (rows == 0 || n == 0) return W4A16_OK;
+  if (num_experts == 0) return W4A16_ERR_SHAPE;
+  if (!y || !offsets) return W4A16_ERR_NULL;
+  if (k > 0 && (!x || !packed || !scales)) return W4A16_ERR_NULL;
+  if (!aligned(y, 16) || !aligned(offsets, 4) ||
+      (k > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) ||
+                 (pair_token && !aligned(pair_token, 4)))))
+    return W4A16_ERR_ALIGN;
+  const int64_t x_rows = pair_token ? tokens : rows;   // without pair_token, x is the sorted rows
+  if (!bank_fits(num_experts, 2 * n, k)) return W4A16_ERR_SHAPE;
+  if (2 * x_rows * k >= kMaxBufferBytes || 2 * rows * n >= kMaxBufferBytes) return W4A16_ERR_SHAPE;
+  DeviceInfo dev;
+  if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(rows * n), st));   // SiLU(0) * 0
+  return status_of(w4a16::launch_grouped_gemm_swiglu(x, pair_token, (int)x_rows, packed, scales, offsets, y,
+                                                     num_experts, (int)rows, (int)n, (int)k, group, dev, st));
+}
+
 w4a16_status w4a16_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t num_experts, int32_t* offsets,
                     int32_t* pair_token, int32_t* pair_row, w4a16_stream_t stream) {
   if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > kMaxRouteExperts) return W4A16_ERR_SHAPE;

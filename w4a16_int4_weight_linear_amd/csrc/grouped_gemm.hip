@@ -33,6 +33,11 @@
 // * Gather variant (launch_grouped_gemm_gather): row r's activations are read
 //   from token pair_token[r] of the unsorted token rows, so the expert-sorted
 //   copy of the activations is never written.
+// * SwiGLU variant (launch_grouped_gemm_swiglu, the experts' fused gate/up
+//   projection): each expert's weight rows interleave gate (even) and up (odd)
+//   rows, so a lane's four consecutive output columns are two whole (gate, up)
+//   pairs, and the epilogue writes SiLU(gate) * up for both (fp32, rounded
+//   once): the 2 x rows x n intermediate never reaches memory.
 #include "device.hpp"
 #include "kernels.hpp"
 #include "launch.hpp"
@@ -132,7 +137,7 @@ __device__ inline bool find_item(const int32_t* __restrict__ offsets, int expert
 // slice lq).  Inside a row the 16-byte slots are XOR-swizzled by (row / 2) so
 // the operand reads hit distinct banks; the swizzle is applied to which piece
 // a lane loads, so the LDS write stays one contiguous 1 KB per instruction.
-template <int G, bool ALIGNED, int MB>
+template <int G, bool ALIGNED, int MB, bool SWIGLU>
 __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed_e,
                                           const uint16_t* __restrict__ scales_e, uint16_t* __restrict__ y,
                                           int N, int K, int rows_total, const Item& it, int band, uint8_t* lds,
@@ -354,6 +359,25 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
     const int r = i * 16 + li;
     const int row = it.row_begin + r;
     if (r >= it.rows || row < 0 || row >= rows_total) continue;
+    if constexpr (SWIGLU) {
+      // columns n0, n0 + 1 and n0 + 2, n0 + 3 are (gate, up) pairs: outputs n0 / 2, n0 / 2 + 1
+      const int no = N >> 1;
+#pragma unroll
+      for (int b = 0; b < kNB; ++b) {
+        const int c0 = (nw + b * 16 + 4 * lq) >> 1;
+        const float g0 = acc[i][b][0], g1 = acc[i][b][2];
+        const uint16_t h0 = float_to_half_bits(g0 / (1.0f + __expf(-g0)) * acc[i][b][1]);
+        const uint16_t h1 = float_to_half_bits(g1 / (1.0f + __expf(-g1)) * acc[i][b][3]);
+        uint16_t* dst = y + (size_t)row * no + c0;
+        if ((no & 1) == 0 && c0 + 1 < no) {
+          *reinterpret_cast<uint32_t*>(dst) = h0 | ((uint32_t)h1 << 16);
+        } else {
+          if (c0 < no) dst[0] = h0;
+          if (c0 + 1 < no) dst[1] = h1;
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const int n0 = nw + b * 16 + 4 * lq;
@@ -372,7 +396,7 @@ __device__ __forceinline__ void item_body(const uint16_t* __restrict__ x, const 
   }
 }
 
-template <int G, bool ALIGNED>
+template <int G, bool ALIGNED, bool SWIGLU>
 __global__ void __launch_bounds__(kThreads)
 grouped_gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                     const uint16_t* __restrict__ scales, const int32_t* __restrict__ offsets,
@@ -393,15 +417,17 @@ grouped_gemm_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__
   const uint32_t* pe = packed + e * (size_t)N * (size_t)(K >> 3);
   const uint16_t* se = scales + e * (size_t)N * (size_t)(K / G);
   if (it.rows > 16)
-    item_body<G, ALIGNED, 2>(x, pe, se, y, N, K, rows_total, it, band, lds, pair_token, x_rows);
+    item_body<G, ALIGNED, 2, SWIGLU>(x, pe, se, y, N, K, rows_total, it, band, lds, pair_token, x_rows);
   else
-    item_body<G, ALIGNED, 1>(x, pe, se, y, N, K, rows_total, it, band, lds, pair_token, x_rows);
+    item_body<G, ALIGNED, 1, SWIGLU>(x, pe, se, y, N, K, rows_total, it, band, lds, pair_token, x_rows);
 }
 
 }  // namespace
 
 namespace {
 
+// n: weight rows per expert (2 x the outputs for SWIGLU)
+template <bool SWIGLU>
 hipError_t launch_grouped(const uint16_t* x, const int32_t* pair_token, int x_rows, const uint32_t* packed,
                           const uint16_t* scales, const int32_t* offsets, uint16_t* y, int experts, int rows, int n,
                           int k, int group, hipStream_t stream) {
@@ -415,8 +441,11 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* pair_token, int x_ro
   // one vector load per row brings a step's scales when every scale row is
   // 16-byte (g32) or 4-byte (g128) aligned in memory
   const uintptr_t sp = reinterpret_cast<uintptr_t>(scales);
-  auto kern = group == 32 ? (spr % 8 == 0 && (sp & 15) == 0 ? grouped_gemm_kernel<32, true> : grouped_gemm_kernel<32, false>)
-                          : (spr % 2 == 0 && (sp & 3) == 0 ? grouped_gemm_kernel<128, true> : grouped_gemm_kernel<128, false>);
+  auto kern = group == 32
+                  ? (spr % 8 == 0 && (sp & 15) == 0 ? grouped_gemm_kernel<32, true, SWIGLU>
+                                                    : grouped_gemm_kernel<32, false, SWIGLU>)
+                  : (spr % 2 == 0 && (sp & 3) == 0 ? grouped_gemm_kernel<128, true, SWIGLU>
+                                                   : grouped_gemm_kernel<128, false, SWIGLU>);
   return launch_kernel(kern, grid, block, 0, stream, x, packed, scales, offsets, y, experts, n, k, rows, bands,
                        pair_token, x_rows);
 }
@@ -426,14 +455,22 @@ hipError_t launch_grouped(const uint16_t* x, const int32_t* pair_token, int x_ro
 hipError_t launch_grouped_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                                const int32_t* offsets, uint16_t* y, int experts, int rows, int n, int k,
                                int group, const DeviceInfo&, hipStream_t stream) {
-  return launch_grouped(x, nullptr, rows, packed, scales, offsets, y, experts, rows, n, k, group, stream);
+  return launch_grouped<false>(x, nullptr, rows, packed, scales, offsets, y, experts, rows, n, k, group, stream);
 }
 
 hipError_t launch_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_token, int tokens,
                                       const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
                                       uint16_t* y, int experts, int rows, int n, int k, int group,
                                       const DeviceInfo&, hipStream_t stream) {
-  return launch_grouped(x, pair_token, tokens, packed, scales, offsets, y, experts, rows, n, k, group, stream);
+  return launch_grouped<false>(x, pair_token, tokens, packed, scales, offsets, y, experts, rows, n, k, group, stream);
+}
+
+hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* pair_token, int x_rows,
+                                      const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
+                                      uint16_t* y, int experts, int rows, int n_out, int k, int group,
+                                      const DeviceInfo&, hipStream_t stream) {
+  return launch_grouped<true>(x, pair_token, x_rows, packed, scales, offsets, y, experts, rows, 2 * n_out, k, group,
+                              stream);
 }
 
 }  // namespace w4a16

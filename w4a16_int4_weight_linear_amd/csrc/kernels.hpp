@@ -76,6 +76,13 @@ hipError_t launch_grouped_gemm_gather(const uint16_t* x, const int32_t* pair_tok
                                       uint16_t* y, int experts, int rows, int n, int k, int group,
                                       const DeviceInfo& dev, hipStream_t stream);
 
+// SwiGLU variant: packed/scales hold 2 n_out interleaved (gate, up) rows per expert;
+// y [rows, n_out] = SiLU(gate) * up.  pair_token may be null (x sorted, x_rows = rows).
+hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* pair_token, int x_rows,
+                                      const uint32_t* packed, const uint16_t* scales, const int32_t* offsets,
+                                      uint16_t* y, int experts, int rows, int n_out, int k, int group,
+                                      const DeviceInfo& dev, hipStream_t stream);
+
 // ---- MoE routing and combine (moe.hip) ----
 size_t moe_route_lds(int experts);
 hipError_t launch_moe_route(const int32_t* ids, int pairs, int topk, int experts, int32_t* offsets,
