@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--traffic-reduce", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the two counter_collection.csv files of the --traffic-probe "
                          "passes into profiles/gemv.traffic.json (host only, no GPU)")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("COUNTER_CSV", "OUT_MD", "COMMAND"),
+                    help="turn a rocprofv3 --pmc counter_collection.csv into a per-kernel, per-workload "
+                         "summary with derived clock, MFMA busy and instructions per MFMA (host only, no GPU)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "COMMAND"),
                     help="turn a rocprofv3 kernel trace of this benchmark into the per-kernel "
                          "summaries profiles/*.kernel_trace.md (host only, no GPU)")
@@ -662,6 +665,66 @@ def trace_summary(trace_csv, command):
         print("wrote", path)
 
 
+XCDS = 8   # MI355X: GRBM counters are reported once per XCD and summed by the profiler
+
+
+def counter_summary(csv_path, out_md, command):
+    """Per-kernel counters of one --pmc pass, split into workloads by the MFMA count.
+
+    Derived: clock = GRBM_GUI_ACTIVE / XCDS / duration (the profiler sums the counter
+    over the XCDs); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GUI cycles per XCD);
+    VALU and LDS instructions per MFMA instruction."""
+    import collections
+    import csv
+    disp = collections.defaultdict(dict)
+    for r in csv.DictReader(open(csv_path)):
+        d = disp[int(r["Dispatch_Id"])]
+        d["kernel"] = r["Kernel_Name"]
+        d["grid"] = r["Grid_Size"]
+        d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    groups = collections.defaultdict(list)
+    for d in disp.values():
+        if d.get("SQ_INSTS_MFMA", 0) <= 0:
+            continue
+        groups[(d["kernel"], d["grid"], round(d["SQ_INSTS_MFMA"], -4))].append(d)
+    simds = 4 * 256
+    lines = ["| kernel | grid | dispatches | mean us | MFMA instr | VALU instr | LDS instr | VALU/MFMA | "
+             "LDS/MFMA | clock GHz | MFMA busy |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (k, g, _), ds in sorted(groups.items(), key=lambda t: t[0][2]):
+        avg = lambda c: sum(d.get(c, 0.0) for d in ds) / len(ds)
+        gui = avg("GRBM_GUI_ACTIVE") / XCDS
+        dur = avg("dur_us")
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (simds * gui) if gui else float("nan")
+        name = k.replace("(anonymous namespace)::", "").replace("void ", "", 1).split("(")[0][:70]
+        lines.append(f"| {name} | {g} | {len(ds)} | {dur:.1f} | {avg('SQ_INSTS_MFMA'):.4g} | "
+                     f"{avg('SQ_INSTS_VALU'):.4g} | {avg('SQ_INSTS_LDS'):.4g} | "
+                     f"{avg('SQ_INSTS_VALU') / avg('SQ_INSTS_MFMA'):.2f} | {avg('SQ_INSTS_LDS') / avg('SQ_INSTS_MFMA'):.2f} | "
+                     f"{gui / dur / 1e3:.2f} | {busy:.3f} |")
+    with open(out_md, "w") as f:
+        f.write("Command (from the repository root on the GPU box), then the summary:\n\n```\n"
+                f"{command}\npython3 bench.py --counter-summary <pmc dir>/pmc_counter_collection.csv {out_md} '<command>'\n```\n\n")
+        f.write("\n".join(lines) + "\n")
+    print("wrote", out_md)
+
+
+def dense_fp16_reference(torch):
+    """The vendor library's dense fp16 GEMM (torch.mm, hipBLASLt) on the prefill shapes:
+    what a dense contraction without any dequantisation sustains on this machine, beside the
+    published 2.5 PFLOP/s.  Calibration only (it reads 4x the weight bytes)."""
+    out = {}
+    k, n = 5120, 17408
+    wt = torch.randn(k, n, dtype=torch.float16, device="cuda")
+    for m in (512, 4096):
+        x = torch.randn(m, k, dtype=torch.float16, device="cuda")
+        y = torch.empty(m, n, dtype=torch.float16, device="cuda")
+        t = per_launch(torch, lambda i: torch.mm(x, wt, out=y), 20 if m == 512 else 5, batches=5)
+        fl = dense_flops(m, n, k)
+        out[f"mm_{m}x{k}x{n}_fp16"] = {"flops": fl, **timing_fields(t, fl, 1e12, "tflops")}
+    del wt
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -820,6 +883,9 @@ def main():
     if args.trace_summary:
         trace_summary(*args.trace_summary)
         return
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1",
                           "reason": "the W4A16 layer is built and measured on a single MI355X"}))
@@ -843,6 +909,8 @@ def main():
                          ("moe_ffn", moe_ffn_component)):
             if name in comps:
                 res[name] = fn(torch, w4, synth, args)
+        if "dense_ref" in comps:
+            res["dense_ref"] = dense_fp16_reference(torch)
         print(json.dumps({"components": res}, default=float))
         return
     decode = decode_component(torch, w4, synth, args)
@@ -897,6 +965,12 @@ def main():
                                                                                   "device.hpp")),
                               "kernel": "gemm_kernel<128, false, true>", "launch_us": round(g["launch_ms"] * 1e3, 3),
                               "flops_per_launch": g["flops"]}
+    if "prefill" in comps:
+        dense = dense_fp16_reference(torch)
+        line["dense_fp16_gemm_reference"] = dense
+        for name, key in (("mm_512x5120x17408_fp16", "gemm_m512"), ("mm_4096x5120x17408_fp16", "gemm_m4096")):
+            if key in rooflines:
+                rooflines[key]["vs_dense_fp16_library"] = round(rooflines[key]["achieved"] / dense[name]["tflops"], 3)
     line["rooflines"] = rooflines
     if "gemm_m512" in rooflines:
         line["gemm_m512"] = rooflines["gemm_m512"]
