@@ -36,7 +36,9 @@ def run_gemm(w4, x, packed, scales, group):
 # data-parallel round plus a stream-K remainder (264 and 260 tiles of 128 x 256).
 EXACT_SHAPES = [(1, 64, 128, 128), (7, 300, 256, 32), (128, 256, 512, 128), (130, 260, 1024, 32),
                 (257, 513, 5120, 128), (64, 100, 96, 32), (300, 1000, 2080, 32), (512, 17408 // 8, 640, 128),
-                (1024, 8448, 256, 128), (640, 13312, 160, 32)]
+                (1024, 8448, 256, 128), (640, 13312, 160, 32),
+                # 256-row tiles (M >= 1024): ragged M and N, a K tail of 32 (g32), unaligned scale rows
+                (1100, 700, 2080, 32), (2048, 513, 640, 128), (1030, 260, 384, 128)]
 
 
 @pytest.mark.parametrize("m,n,k,group", EXACT_SHAPES)
