@@ -10,7 +10,7 @@ GemvPlan gemv_plan(int, int, int, int, const DeviceInfo&, bool) { return GemvPla
 int64_t gemv_max_k(int, int, const DeviceInfo&) { return 0; }
 hipError_t launch_gemv(const uint16_t*, const uint32_t*, const uint16_t*, uint16_t*, int, int, int, int,
                        const GemvPlan&, const DeviceInfo&, hipStream_t) { return hipErrorNoDevice; }
-bool gemv_mfma_plan(int, int, int, const DeviceInfo&, int*, size_t*, bool) { return false; }
+bool gemv_mfma_plan(int, int, int, int, const DeviceInfo&, int*, size_t*, bool) { return false; }
 hipError_t launch_gemv_mfma(const uint16_t*, const uint32_t*, const uint16_t*, uint16_t*, int, int, int, int, int,
                             size_t, const DeviceInfo&, hipStream_t, bool) { return hipErrorNoDevice; }
 bool gemm_skinny_fits(int, int, int, const DeviceInfo&) { return false; }

@@ -95,7 +95,7 @@ GemmPath gemm_path(int64_t m, int64_t n, int64_t k, int32_t group, const DeviceI
   if (m <= 4) {
     int mb = 0;
     size_t mlds = 0;
-    if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, dev, &mb, &mlds)) return GemmPath::kGemv;
+    if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, group, dev, &mb, &mlds)) return GemmPath::kGemv;
     if (w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev).ok) return GemmPath::kGemv;
   }
   if (m <= 32 && w4a16::gemm_skinny_fits((int)(m < 16 ? m : 16), (int)n, (int)k, dev)) return GemmPath::kSkinny;
@@ -122,7 +122,7 @@ int gemv_dispatch(const uint16_t* x, const uint32_t* packed, const uint16_t* sca
   // per-lane kernel is), while its activations fit in LDS.
   int mb = 0;
   size_t mlds = 0;
-  if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, dev, &mb, &mlds))
+  if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, group, dev, &mb, &mlds))
     return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)n, (int)k, group, mb, mlds, dev, st));
   const w4a16::GemvPlan plan = w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev);
   if (!plan.ok) return -1;
@@ -274,7 +274,7 @@ w4a16_status w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const 
   // four rows on MFMA, as for the plain product), while the activations fit in LDS.
   int mb = 0;
   size_t mlds = 0;
-  if (m >= 3 && m <= 4 && w4a16::gemv_mfma_plan((int)m, (int)(2 * n), (int)k, dev, &mb, &mlds, true))
+  if (m >= 3 && m <= 4 && w4a16::gemv_mfma_plan((int)m, (int)(2 * n), (int)k, group, dev, &mb, &mlds, true))
     return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)(2 * n), (int)k, group, mb, mlds,
                                              dev, st, true));
   if (m <= 4) {

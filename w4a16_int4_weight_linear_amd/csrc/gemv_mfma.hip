@@ -2,28 +2,49 @@
 //
 // y[m, n] = sum_k x[m, k] * s[n, k / g] * q[n, k] for a few activation rows:
 // the np4 column of the LLM170 CUDA/W4A16 page's benchmark tables, where the
-// rows of a decode batch share one pass over the weights.  The per-lane dot
-// product kernel (gemv.hip) reads 32 activations per activation row from LDS
-// for every 32 weights, so at M = 4 LDS bandwidth, not HBM, sets its speed.
-// Here the contraction runs on v_mfma_f32_16x16x32_f16 with the weights as the
-// A operand (16 weight rows x 32 k) and the activations as the B operand
-// (16 columns, of which the first M are real): one 16-byte activation fragment
-// now serves 16 weight rows.
+// rows of a decode batch share one pass over the weights.  The product is a
+// weight stream like the M = 1 decode step (gemv.hip), but reading M rows of
+// activations for every weight from LDS would cost M times the LDS traffic, so
+// the contraction runs on the matrix cores.
 //
-// * Work split as in the per-lane kernel: each workgroup owns a contiguous
-//   range of weight rows (range sizes differ by at most one row).  The range is
-//   covered by 16-row blocks; a unit of work is (block, line) where a line is
-//   256 k, i.e. 128 bytes of every row.  The workgroup's eight waves take the
-//   units round robin and keep one fp32 accumulator tile per block.
-// * Weight loads cover whole 128-byte lines (8 rows x 128 bytes per load
-//   instruction), go through a per-wave LDS tile into operand layout, and are
-//   dequantised in registers (nibble -> fp16 code -> times the group scale).
-//   kDepth units are in flight ahead of use.
-// * The activations (M rows, all of K) are staged in LDS once per workgroup.
-// * At the end the eight waves' accumulators meet in LDS and are added in wave
-//   order (deterministic), rounded once to fp16 and stored.
+// * The instruction is v_mfma_f32_4x4x4_16b_f16: sixteen independent 4 x 4 x 4
+//   products per wave, block b in lanes 4b .. 4b + 3.  The activations are the
+//   A operand (row i of a block: activation row i, of which the first M are
+//   real) and the weights the B operand (column j of a block: one weight row).
+//   Its operand layout is what lets a weight load cover whole 128-byte lines:
+//   the four lanes of a block need four different weight rows at the same k,
+//   so one 16-byte-per-lane load gives lane l row (l & 3) + 4 (l >> 5) and
+//   32-k chunk (l >> 2) & 7 of a 256-k line -- 8 rows x 128 contiguous bytes.
+//   (With a 16 x 16 product the sixteen columns of one load would be sixteen
+//   rows, 64 bytes each: half lines, which this part reads markedly slower.)
+// * Each lane's 16 bytes (32 k) feed 8 MFMAs of 4 k.  Since 32 divides the
+//   group size, a lane's 32 k lie in one quantisation group: the codes enter
+//   the MFMA as the fp16 values 1024 + u (one mask and two byte permutes per
+//   pair, exact), the 8 MFMAs give t = sum x (1024 + u) over the chunk, and
+//   the scale and the offset are applied once per chunk on the four
+//   accumulators: acc += s * (t - 1032 * sum x).  This is exact for integer
+//   data and the same for every group size.
+// * Work split: each workgroup (one per CU) owns a contiguous range of weight
+//   rows (sizes differ by at most one row), covered by 8-row blocks.  Its units
+//   (block, line) are dealt to the waves as contiguous runs in block-major
+//   order, so every wave streams along its rows with several loads in flight,
+//   like the M = 1 kernel's flat streams.
+// * The activations are staged in LDS once per workgroup, each group of 8 k in
+//   the order the dequantisation produces (k = 0, 4, 2, 6, 1, 5, 3, 7), with
+//   the sum of every 32-k chunk per row; the workgroup's scales are staged
+//   beside them.  Lanes whose A row is not a real activation row read row
+//   i mod M, whose results are never stored.
+// * When a wave leaves a block, the eight lanes holding the chunks of one row
+//   are added (DPP and one swizzle) and the row's partial sums go to LDS; at
+//   the end the waves' partials are added in wave order (deterministic),
+//   rounded once to fp16 and stored.
+// * Gated variant (the SwiGLU gate/up pair of an FFN): the weight rows
+//   interleave gate and up rows, workgroups own whole pairs, and the final
+//   step writes SiLU(gate) * up for each pair.
+//
+// For integer activations, codes and power-of-two scales every product and
+// partial sum is exact, so such inputs give bit-exact results.
 #include <atomic>
-#include <type_traits>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -33,232 +54,266 @@
 namespace w4a16 {
 namespace {
 
-#ifndef W4A16_GEMVM_DEPTH
-#define W4A16_GEMVM_DEPTH 1
+#ifndef W4A16_NP4_THREADS
+#define W4A16_NP4_THREADS 1024
 #endif
-#ifndef W4A16_GEMVM_WG_PER_CU
-#define W4A16_GEMVM_WG_PER_CU 2
+#ifndef W4A16_NP4_LOADS_IN_FLIGHT
+#define W4A16_NP4_LOADS_IN_FLIGHT 4
 #endif
-constexpr int kThreads = 512;
+#ifndef W4A16_NP4_WG_PER_CU
+#define W4A16_NP4_WG_PER_CU 1
+#endif
+constexpr int kThreads = W4A16_NP4_THREADS;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxBlocks = 4;                   // 16-row blocks per workgroup
+constexpr int kDepth = W4A16_NP4_LOADS_IN_FLIGHT;   // loads in flight per wave
 constexpr int KL = 256;                         // k per line: 128 bytes of a weight row
-constexpr int kDepth = W4A16_GEMVM_DEPTH;       // units in flight ahead of use
-static_assert(kDepth == 1, "the unit loop refills its single ring slot");
-constexpr int kTileWave = 16 * 128;             // per-wave transpose tile [16 rows][128 B]
-constexpr int kTileBytes = kWaves * kTileWave;
+constexpr int kRows = 8;                        // weight rows per block (one load)
+constexpr int kMaxBlocks = 32;                  // blocks per workgroup
+constexpr uint32_t kScaleSlack = 256;           // staged past the workgroup's last scale
 
-// Staged activation rows are padded with zeros to whole lines (the operand
-// reads of a line's last chunk reach its end), plus 16 bytes so consecutive
-// rows start on different banks.
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Staged activation rows hold whole lines (zeros past K) plus 16 bytes, so
+// consecutive rows start on different banks.
 __host__ __device__ inline uint32_t x_pitch(int k) { return (uint32_t)((k + KL - 1) / KL) * KL * 2u + 16u; }
-// LDS: [activations M x pitch][tiles]; the end-of-kernel partial sums reuse the front.
-__host__ inline size_t lds_bytes(int m, int k, int blocks) {
-  const size_t main = (size_t)m * x_pitch(k) + kTileBytes;
-  (void)blocks;
-  const size_t red = (size_t)kWaves * kMaxBlocks * 1024;   // [wave][block][lane] partial tiles
-  return main > red ? main : red;
+
+struct Layout {
+  uint32_t xs, xsum, sc, red, total;            // byte offsets of the LDS regions, and the size
+};
+// m activation rows of k, a workgroup of `rows` weight rows with spr scales each.
+__host__ __device__ inline Layout lds_layout(int m, int k, int spr, int rows) {
+  Layout l;
+  const int lines = (k + KL - 1) / KL;
+  const int nb = (rows + kRows - 1) / kRows;
+  l.xs = 0;
+  l.xsum = (uint32_t)m * x_pitch(k);
+  l.sc = l.xsum + (uint32_t)lines * 8u * 16u;   // [32-k chunk][4 rows] fp32
+  l.red = l.sc + (((uint32_t)rows * (uint32_t)spr * 2u + 15u) & ~15u) + 32u + kScaleSlack;
+  l.total = l.red + (uint32_t)(kWaves * nb * kRows) * 16u;
+  return l;
 }
 
-// GATED: the N weight rows interleave the gate and up rows of a SwiGLU pair;
-// workgroups own whole pairs (rows_base / rows_extra count pairs) and
-// y[m, N / 2] = SiLU(gate) * up.
-template <int M, int G, bool ALIGNED, bool GATED>
+// The eight codes of packed word q as the fp16 values 1024 + u, in the order
+// (0, 4), (2, 6), (1, 5), (3, 7) of dequant_word (exact; no offset, no scale).
+__device__ inline u32x4 codes_1024(uint32_t q) {
+  const uint32_t magic = 0x64646464u;
+  const uint32_t qa = q & 0x0F0F0F0Fu;            // bytes u0 u2 u4 u6
+  const uint32_t qb = (q >> 4) & 0x0F0F0F0Fu;     // bytes u1 u3 u5 u7
+  return u32x4{__builtin_amdgcn_perm(magic, qa, 0x04020400u), __builtin_amdgcn_perm(magic, qa, 0x04030401u),
+               __builtin_amdgcn_perm(magic, qb, 0x04020400u), __builtin_amdgcn_perm(magic, qb, 0x04030401u)};
+}
+
+__device__ inline f16x4 as_h4(uint32_t a, uint32_t b) { return __builtin_bit_cast(f16x4, u32x2{a, b}); }
+
+// rows_base / rows_extra count row units: single rows, or (gate, up) row pairs
+// (GATED).  `scales` is rounded down to 16 bytes by the launcher and sc_shift
+// bytes added back here, so the 16-byte staging loads are aligned in memory.
+template <int M, int G, bool GATED>
 __global__ void __launch_bounds__(kThreads)
 gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                  const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
-                 int N, int K, int rows_base, int rows_extra) {
+                 int N, int K, int rows_base, int rows_extra, uint32_t sc_shift) {
   constexpr int kUnit = GATED ? 2 : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lq = lane >> 4;
-  const int li = lane & 15;
+  const int lr = (lane & 3) + 4 * (lane >> 5);    // weight row of the block (B column)
+  const int lc = (lane >> 2) & 7;                 // 32-k chunk of the line
+  const int li = lane & 3;                        // A row of the 4 x 4 block
 
   const int blk = blockIdx.x;
   const int nr = kUnit * (rows_base + (blk < rows_extra ? 1 : 0));
   const int r0 = kUnit * (blk * rows_base + (blk < rows_extra ? blk : rows_extra));
-  const int nb = (nr + 15) >> 4;                  // 16-row blocks (<= kMaxBlocks, checked on the host)
+  const int nb = (nr + kRows - 1) / kRows;        // blocks (<= kMaxBlocks, checked on the host)
   const int lines = (K + KL - 1) / KL;
   const int units = nb * lines;
-
-  const uint32_t row_w = (uint32_t)K >> 1;
-  const uint32_t spr = (uint32_t)(K / G);
-  // descriptors cover exactly the workgroup's rows: rows past the range read zero
-  const __amdgpu_buffer_rsrc_t wres =
-      make_rsrc(reinterpret_cast<const uint8_t*>(packed) + (size_t)r0 * row_w, (uint32_t)nr * row_w);
-  const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales + (size_t)r0 * spr, (uint32_t)nr * spr * 2u);
+  const int spr = K / G;
+  const Layout L = lds_layout(M, K, spr, kUnit * (rows_base + (rows_extra ? 1 : 0)));
   const uint32_t xp = x_pitch(K);
 
-  // ---- whole-line loads: instruction i reads rows 8 i .. 8 i + 7 of the block ----
-  uint32_t woff[2];
-  int klim[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * i + (lane >> 3);
-    const int q = (lane & 7) ^ ((r >> 1) & 7);
-    woff[i] = (uint32_t)r * row_w + 16u * (uint32_t)q;
-    klim[i] = K - 32 * q;
-  }
-  // The whole offset is in the vector offset, so the descriptor's range check
-  // covers it: rows past the workgroup's range read zero.
-  auto load_raw = [&](int b, int s, int i) -> u32x4 {
-    const uint32_t off = KL * s < klim[i] ? woff[i] + 16u * (uint32_t)b * row_w + 128u * (uint32_t)s : kOutOfRange;
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kStream));
-  };
-  uint8_t* tile = smem + (size_t)M * xp + wave * kTileWave;
-  uint8_t* tile_w = tile + 16 * lane;
-  const uint32_t swz = (uint32_t)((li >> 1) & 7);
-  const uint8_t* tile_r0 = tile + li * 128 + 16 * ((uint32_t)lq ^ swz);
-  const uint8_t* tile_r1 = tile + li * 128 + 16 * ((uint32_t)(4 + lq) ^ swz);
-
-  // ---- scales of operand column li of block b ----
-  const uint32_t scol = (uint32_t)li * spr * 2u;
-  auto srow = [&](int b) { return scol + 16u * (uint32_t)b * spr * 2u; };
-  auto load_s32 = [&](int b, int s) -> u32x4 {       // G = 32 aligned: groups 8 s .. 8 s + 7
-    const uint32_t off = 8 * s < (int)spr ? srow(b) + 16u * (uint32_t)s : kOutOfRange;
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0));
-  };
-  auto load_s128 = [&](int b, int s) -> uint32_t {   // G = 128 aligned: groups 2 s, 2 s + 1
-    const uint32_t off = 2 * s < (int)spr ? srow(b) + 4u * (uint32_t)s : kOutOfRange;
-    return __builtin_amdgcn_raw_buffer_load_b32(sres, off, 0, 0);
-  };
-  auto load_s16 = [&](int b, int s, int h) -> uint32_t {   // any alignment: k = 256 s + 128 h + 32 lq
-    const int k = KL * s + 128 * h + 32 * lq;
-    const uint32_t off = k < K ? srow(b) + 2u * (uint32_t)(k / G) : kOutOfRange;
-    return __builtin_amdgcn_raw_buffer_load_b16(sres, off, 0, 0);
-  };
-
-  struct Slot {
-    u32x4 raw[2];
-    u32x4 s32;
-    uint32_t s128;
-    uint32_t s16[2];
-  };
-  Slot ring[kDepth];
-  auto issue = [&](int u, Slot& sl) {
-    const int b = u < units ? u / lines : 0;
-    const int s = u < units ? u - b * lines : lines;   // past the end: s = lines, no memory access
-    sl.raw[0] = load_raw(b, s, 0);
-    sl.raw[1] = load_raw(b, s, 1);
-    if constexpr (ALIGNED && G == 32) sl.s32 = load_s32(b, s);
-    if constexpr (ALIGNED && G == 128) sl.s128 = load_s128(b, s);
-    if constexpr (!ALIGNED) { sl.s16[0] = load_s16(b, s, 0); sl.s16[1] = load_s16(b, s, 1); }
-  };
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) issue(wave + kWaves * d, ring[d]);
-
-  // ---- stage the activations (all of K, nibble-pair order within each 8; zeros to the line end) ----
-  // Batches of kXBatch loads per thread are issued before any is written, so
-  // the staging costs one memory latency per batch rather than one per piece.
-  const int row_pieces = lines * (KL / 8);
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-  constexpr int kXBatch = 8;
-  for (int p0 = tid; p0 < M * row_pieces; p0 += kXBatch * kThreads) {
-    u32x4 v[kXBatch];
-#pragma unroll
-    for (int j = 0; j < kXBatch; ++j) {
-      const int p = p0 + j * kThreads;
-      const int m = p / row_pieces;
-      const int c = p - m * row_pieces;
-      const bool ok = p < M * row_pieces && c < (K >> 3);
-      v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          xres, ok ? ((uint32_t)m * (uint32_t)K + (uint32_t)c * 8u) * 2u : kOutOfRange, 0, 0));
+  // ---- this wave's units [u0, u1) and its first loads ----
+  const int u0 = (int)((int64_t)units * wave / kWaves), u1 = (int)((int64_t)units * (wave + 1) / kWaves);
+  const uint32_t row_w = (uint32_t)K >> 1;
+  // the descriptor covers exactly the workgroup's rows: rows past its range read zero
+  const __amdgpu_buffer_rsrc_t wres =
+      make_rsrc(reinterpret_cast<const uint8_t*>(packed) + (size_t)r0 * row_w, (uint32_t)nr * row_w);
+  const uint32_t w_v = (uint32_t)lr * row_w + 16u * (uint32_t)lc;
+  // on the last line, chunks that start at or past K load nothing (zeros)
+  const bool tail_ok = KL * (lines - 1) + 32 * lc < K;
+  const uint32_t w_v_tail = tail_ok ? w_v : kOutOfRange;
+  // cursors (wave-uniform): the next unit to load is (ib, is), line-minor
+  const int b_first = u0 / lines, s_first = u0 - b_first * lines;
+  int iu = u0, ib = b_first, is = s_first;
+  u32x4 ring[kDepth];
+  auto issue = [&](int slot) {
+    if (iu < u1) {
+      ring[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          wres, is == lines - 1 ? w_v_tail : w_v, (uint32_t)(kRows * ib) * row_w + 128u * (uint32_t)is, kStream));
     }
-#pragma unroll
-    for (int j = 0; j < kXBatch; ++j) {
-      const int p = p0 + j * kThreads;
-      const int m = p / row_pieces;
-      const int c = p - m * row_pieces;
-      if (p < M * row_pieces) *reinterpret_cast<u32x4*>(smem + (size_t)m * xp + (size_t)c * 16) = permute_a(v[j]);
+    ++iu;
+    if (++is == lines) {
+      is = 0;
+      ++ib;
     }
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) issue(d);
+
+  // ---- stage the activations (and their 32-k sums), the scales, zero partials ----
+  {
+    // chunk c of row m: 8 k, stored permuted; 4 consecutive chunks (lanes) are one 32-k sum
+    const int chunks = lines * (KL / 8);
+    const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    // scales of the workgroup's rows, 16-byte chunks from an aligned start; the
+    // first chunk of each thread is loaded here, under the activation loads
+    const uint32_t sc_begin = (uint32_t)r0 * (uint32_t)spr * 2u + sc_shift;
+    const uint32_t sc_a0 = sc_begin & ~15u;
+    const uint32_t sc_bytes = (uint32_t)N * (uint32_t)spr * 2u + sc_shift;
+    const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, sc_bytes);
+    const uint32_t sc_chunks = (sc_begin - sc_a0 + (uint32_t)nr * (uint32_t)spr * 2u + 15u) >> 4;
+    u32x4 sc_first = u32x4{};
+    if ((uint32_t)tid < sc_chunks) sc_first = load16_tail(sres, sc_a0 + (uint32_t)tid * 16u, sc_bytes);
+    constexpr int kBatch = 4;
+    for (int p0 = tid; p0 < M * chunks; p0 += kBatch * kThreads) {
+      u32x4 v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int p = p0 + j * kThreads;
+        const int m = p / chunks, c = p - (p / chunks) * chunks;
+        const bool ok = p < M * chunks && 8 * c < K;
+        v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            xres, ok ? ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)c) * 2u : kOutOfRange, 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int p = p0 + j * kThreads;
+        const int m = p / chunks, c = p - (p / chunks) * chunks;
+        if (p < M * chunks)
+          *reinterpret_cast<u32x4*>(smem + L.xs + (uint32_t)m * xp + 16u * (uint32_t)c) = permute_a(v[j]);
+        // the 32-k sum over 4 chunks, which are 4 consecutive lanes (one DPP quad;
+        // chunks per row are a multiple of 4 and so is the thread count)
+        const uint32_t one2 = 0x3C003C00u;   // fp16 pair (1, 1)
+        float sum = dot2(v[j].x, one2, 0.f);
+        sum = dot2(v[j].y, one2, sum);
+        sum = dot2(v[j].z, one2, sum);
+        sum = dot2(v[j].w, one2, sum);
+        sum = dpp_add<0xB1>(sum);    // quad_perm [1,0,3,2]
+        sum = dpp_add<0x4E>(sum);    // quad_perm [2,3,0,1]
+        if (p < M * chunks && (c & 3) == 0) reinterpret_cast<float*>(smem + L.xsum)[(c >> 2) * 4 + m] = sum;
+      }
+    }
+    if ((uint32_t)tid < sc_chunks) *reinterpret_cast<u32x4*>(smem + L.sc + (uint32_t)tid * 16u) = sc_first;
+    for (uint32_t t = tid + kThreads; t < sc_chunks; t += kThreads)
+      *reinterpret_cast<u32x4*>(smem + L.sc + t * 16u) = load16_tail(sres, sc_a0 + t * 16u, sc_bytes);
+    for (uint32_t t = tid; t < (uint32_t)(kWaves * nb * kRows); t += kThreads)
+      reinterpret_cast<f32x4*>(smem + L.red)[t] = f32x4{};
   }
   __syncthreads();
 
-  f32x4 acc[kMaxBlocks];
+  // ---- main loop over this wave's units ----
+  // A operand: activation row li mod M, the lane's chunk (lanes of other rows read the same addresses)
+  const uint8_t* xa = smem + L.xs + (uint32_t)(li % M) * xp + 64u * (uint32_t)lc;
+  const uint8_t* xsa = smem + L.xsum + 16u * (uint32_t)lc;
+  // this lane's scales: row lr of each block
+  const uint8_t* scb = smem + L.sc + (((uint32_t)r0 * (uint32_t)spr * 2u + sc_shift) & 15u) + 2u * (uint32_t)(lr * spr);
+  f32x4 acc = f32x4{};
+  // consume cursor (b, s); a block's partial sums go to LDS after its last
+  // line, or at the end if the wave stops inside the block
+  int b = b_first, s = s_first;
+  auto flush = [&]() {
+    // add the eight chunk lanes of each row: lane bits 2, 3 (DPP), then bit 4
+    f32x4 v = acc;
 #pragma unroll
-  for (int b = 0; b < kMaxBlocks; ++b) acc[b] = f32x4{};
-  const uint32_t sel_lq = (uint32_t)(2 * lq) * 0x00010001u + (uint32_t)(2 * lq + 1) * 0x01000100u;
-  // B operand: activation row li mod M (lanes li >= M give output columns that
-  // are never stored; their duplicate addresses cost no extra LDS bandwidth)
-  const uint8_t* xfrag = smem + (size_t)(li % M) * xp + 64 * lq;
-
-  // One unit (block b, line s) from ring slot `sl` into the accumulator tile `a`.
-  auto unit = [&](int b, int s, Slot& sl, f32x4& a, int u_next) {
-    *reinterpret_cast<u32x4*>(tile_w) = sl.raw[0];
-    *reinterpret_cast<u32x4*>(tile_w + 1024) = sl.raw[1];
-    const u32x4 wq0 = *reinterpret_cast<const u32x4*>(tile_r0);
-    const u32x4 wq1 = *reinterpret_cast<const u32x4*>(tile_r1);
-    f16x2 sv[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if constexpr (!ALIGNED) {
-        const _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)sl.s16[h]);
-        sv[h] = f16x2{v, v};
-      } else if constexpr (G == 32) {
-        sv[h] = h ? __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sl.s32.w, sl.s32.z, sel_lq))
-                  : __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sl.s32.y, sl.s32.x, sel_lq));
-      } else {
-        sv[h] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sl.s128, sl.s128, h ? 0x03020302u : 0x01000100u));
-      }
+    for (int i = 0; i < 4; ++i) {
+      float t = dpp_add<0x124>(v[i]);   // row_ror:4
+      t = dpp_add<0x128>(t);            // row_ror:8
+      t += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));   // lane ^ 16
+      v[i] = t;
     }
-    issue(u_next, sl);   // refill the slot (past the end: no memory access)
-    const uint8_t* xb = xfrag + 512 * s;
+    if (lc == 0) reinterpret_cast<f32x4*>(smem + L.red)[(wave * nb + b) * kRows + lr] = v;
+    acc = f32x4{};
+  };
+  auto consume = [&](const u32x4& wv) {
+    const uint8_t* xs = xa + 512u * (uint32_t)s;
+    u32x4 xf[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x4 wv = h ? wq1 : wq0;
+    for (int w = 0; w < 4; ++w) xf[w] = *reinterpret_cast<const u32x4*>(xs + 16 * w);
+    f32x4 t = f32x4{};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(xb + 256 * h + 16 * w));
-        const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
-        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(q, sv[h]), xf, a, 0, 0, 0);
-      }
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
+      const u32x4 c = codes_1024(q);
+      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].x, xf[w].y), as_h4(c.x, c.y), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].z, xf[w].w), as_h4(c.z, c.w), t, 0, 0, 0);
+    }
+    // the lane's chunk is one group; rows past the workgroup's range and chunks
+    // past K (zero weights) take scale 0
+    const int kc = KL * s + 32 * lc;
+    const bool ok = lr < nr - kRows * b && kc < K;
+    const float sc =
+        ok ? half_bits_to_float(*reinterpret_cast<const uint16_t*>(scb + 2 * (kRows * b * spr + kc / G))) : 0.f;
+    const f32x4 xsum = *reinterpret_cast<const f32x4*>(xsa + 128u * (uint32_t)s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, __builtin_fmaf(-1032.f, xsum[i], t[i]), acc[i]);
+    if (++s == lines) {
+      flush();
+      s = 0;
+      ++b;
     }
   };
-  // The wave's units in order (u = wave, wave + 8, ...), grouped by block so
-  // each block's tile is a fixed register set.
-  int u = wave;
+  int u = u0;
+  for (; u + kDepth <= u1; u += kDepth) {
 #pragma unroll
-  for (int bb = 0; bb < kMaxBlocks; ++bb) {
-    for (; u < units && u < (bb + 1) * lines; u += kWaves) unit(bb, u - bb * lines, ring[0], acc[bb], u + kWaves);
+    for (int d = 0; d < kDepth; ++d) {
+      consume(ring[d]);
+      issue(d);
+    }
   }
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (u + d < u1) consume(ring[d]);
+  if (s != 0) flush();
 
-  // ---- combine the waves' partial tiles in wave order, round once, store ----
-  __syncthreads();                                 // activations and tiles no longer read
-  f32x4* red = reinterpret_cast<f32x4*>(smem);     // [wave][block][lane]
-#pragma unroll
-  for (int bb = 0; bb < kMaxBlocks; ++bb)
-    if (bb < nb) red[(wave * kMaxBlocks + bb) * 64 + lane] = acc[bb];
+  // ---- add the waves' partials in wave order, round once, store ----
   __syncthreads();
-  if (wave < nb && li < M) {
-    f32x4 t = red[wave * 64 + lane];
-    for (int w = 1; w < kWaves; ++w) t += red[(w * kMaxBlocks + wave) * 64 + lane];
-    // lane holds weight rows 4 lq .. 4 lq + 3 of block `wave` for activation row li
-    if constexpr (GATED) {
-      // r0 and nr are even, so rows 4 lq + j, 4 lq + j + 1 are one (gate, up) pair
-#pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        const int rr = 16 * wave + 4 * lq + j;
-        const float g = t[j];
-        if (rr < nr) y[(size_t)li * (N >> 1) + ((r0 + rr) >> 1)] = float_to_half_bits(g / (1.f + __expf(-g)) * t[j + 1]);
+  const f32x4* red = reinterpret_cast<const f32x4*>(smem + L.red);
+  if constexpr (GATED) {
+    // rows (2i, 2i + 1) of a block are one (gate, up) pair
+    for (int t = tid; t < nb * (kRows / 2); t += kThreads) {
+      const int bb = t / (kRows / 2), c = 2 * (t % (kRows / 2));
+      f32x4 g = red[bb * kRows + c], v = red[bb * kRows + c + 1];
+      for (int w = 1; w < kWaves; ++w) {
+        g += red[(w * nb + bb) * kRows + c];
+        v += red[(w * nb + bb) * kRows + c + 1];
       }
-    } else {
+      const int row = kRows * bb + c;
+      if (row < nr) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = 16 * wave + 4 * lq + j;
-        if (rr < nr) y[(size_t)li * N + r0 + rr] = float_to_half_bits(t[j]);
+        for (int m = 0; m < M; ++m)
+          y[(size_t)m * (N >> 1) + ((r0 + row) >> 1)] = float_to_half_bits(g[m] / (1.f + __expf(-g[m])) * v[m]);
+      }
+    }
+  } else {
+    for (int t = tid; t < nb * kRows; t += kThreads) {
+      const int bb = t / kRows, c = t % kRows;
+      f32x4 v = red[bb * kRows + c];
+      for (int w = 1; w < kWaves; ++w) v += red[(w * nb + bb) * kRows + c];
+      const int row = kRows * bb + c;
+      if (row < nr) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) y[(size_t)m * N + r0 + row] = float_to_half_bits(v[m]);
       }
     }
   }
 }
 
-template <int M, int G, bool ALIGNED, bool GATED>
+template <int M, int G, bool GATED>
 hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
                     int blocks, size_t lds, const DeviceInfo& dev, hipStream_t stream) {
   static std::atomic<uint64_t> attr_set{0};   // one bit per device
   const uint64_t bit = 1ull << (dev.device & 63);
-  auto kern = gemv_mfma_kernel<M, G, ALIGNED, GATED>;
+  auto kern = gemv_mfma_kernel<M, G, GATED>;
   if (!(attr_set.load(std::memory_order_acquire) & bit)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
@@ -266,42 +321,35 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* s
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
   const int units = GATED ? n / 2 : n;
-  return launch_kernel(kern, dim3(blocks), dim3(kThreads), lds, stream, x, packed, scales, y, n, k, units / blocks,
-                       units % blocks);
+  const uint32_t sc_shift = (uint32_t)(reinterpret_cast<uintptr_t>(scales) & 15u);
+  const uint16_t* sc_aligned = reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(scales) - sc_shift);
+  return launch_kernel(kern, dim3(blocks), dim3(kThreads), lds, stream, x, packed, sc_aligned, y, n, k,
+                       units / blocks, units % blocks, sc_shift);
 }
 
 template <int M, bool GATED>
 hipError_t launch_g(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
                     int group, int blocks, size_t lds, const DeviceInfo& dev, hipStream_t stream) {
-  const int spr = k / group;
-  // one vector load per row brings a line's scales when every scale row is
-  // 16-byte (g32) or 4-byte (g128) aligned in memory
-  const uintptr_t sp = reinterpret_cast<uintptr_t>(scales);
-  if (group == 32)
-    return spr % 8 == 0 && (sp & 15) == 0
-               ? launch_m<M, 32, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
-               : launch_m<M, 32, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
-  return spr % 2 == 0 && (sp & 3) == 0
-             ? launch_m<M, 128, true, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
-             : launch_m<M, 128, false, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
+  return group == 32 ? launch_m<M, 32, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
+                     : launch_m<M, 128, GATED>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
 }
 
 }  // namespace
 
-bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, size_t* lds, bool gated) {
-  if (m < 2 || m > 4 || n <= 0 || k <= 0) return false;
+bool gemv_mfma_plan(int m, int n, int k, int group, const DeviceInfo& dev, int* blocks, size_t* lds, bool gated) {
+  if (m < 2 || m > 4 || n <= 0 || k <= 0 || (group != 32 && group != 128)) return false;
   // Rows are handed out in units: single rows, or (gate, up) row pairs.
   const int unit = gated ? 2 : 1;
   if (n % unit) return false;
   const int units = n / unit;
-  // Two workgroups per CU, more if a workgroup would exceed kMaxBlocks row blocks.
-  int g = W4A16_GEMVM_WG_PER_CU * dev.num_cu;
-  if ((int64_t)g * 16 > n) g = (n + 15) / 16;
-  const int per = 16 * kMaxBlocks / unit;
+  // W4A16_NP4_WG_PER_CU workgroups per CU, more if a workgroup would exceed
+  // kMaxBlocks row blocks.
+  int g = dev.num_cu * W4A16_NP4_WG_PER_CU;
+  const int per = kRows * kMaxBlocks / unit;
   if ((int64_t)g * per < units) g = (units + per - 1) / per;
   if (g > units) g = units;
   const int rows_max = unit * (units / g + (units % g ? 1 : 0));
-  const size_t bytes = lds_bytes(m, k, (rows_max + 15) / 16);
+  const size_t bytes = lds_layout(m, k, k / group, rows_max).total;
   if (bytes > dev.max_lds) return false;
   *blocks = g;
   *lds = bytes;

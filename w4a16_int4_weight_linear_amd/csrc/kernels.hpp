@@ -38,7 +38,8 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t
 // ---- batched decode GEMV on MFMA, 2 <= m <= 4 (gemv_mfma.hip) ----
 // Workgroup count and LDS bytes; false if the activations do not fit in LDS.
 // gated: the n weight rows interleave SwiGLU gate and up rows and y[m, n / 2] = SiLU(gate) * up.
-bool gemv_mfma_plan(int m, int n, int k, const DeviceInfo& dev, int* blocks, size_t* lds, bool gated = false);
+bool gemv_mfma_plan(int m, int n, int k, int group, const DeviceInfo& dev, int* blocks, size_t* lds,
+                    bool gated = false);
 hipError_t launch_gemv_mfma(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int m,
                             int n, int k, int group, int blocks, size_t lds, const DeviceInfo& dev,
                             hipStream_t stream, bool gated = false);
