@@ -55,7 +55,7 @@ namespace w4a16 {
 namespace {
 
 #ifndef W4A16_NP4_THREADS
-#define W4A16_NP4_THREADS 1024
+#define W4A16_NP4_THREADS 512
 #endif
 #ifndef W4A16_NP4_LOADS_IN_FLIGHT
 #define W4A16_NP4_LOADS_IN_FLIGHT 4
@@ -146,11 +146,14 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   const int b_first = u0 / lines, s_first = u0 - b_first * lines;
   int iu = u0, ib = b_first, is = s_first;
   u32x4 ring[kDepth];
+  // Every slot is loaded unconditionally, in a fixed order, so the compiler can
+  // wait for each load alone (vmcnt); a load past the wave's units has an
+  // out-of-range offset and a zero scalar offset: it touches no memory.
   auto issue = [&](int slot) {
-    if (iu < u1) {
-      ring[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          wres, is == lines - 1 ? w_v_tail : w_v, (uint32_t)(kRows * ib) * row_w + 128u * (uint32_t)is, kStream));
-    }
+    const bool live = iu < u1;
+    const uint32_t voff = !live ? kOutOfRange : (is == lines - 1 ? w_v_tail : w_v);
+    ring[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        wres, voff, live ? (uint32_t)(kRows * ib) * row_w + 128u * (uint32_t)is : 0u, kStream));
     ++iu;
     if (++is == lines) {
       is = 0;
@@ -174,33 +177,37 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
     const uint32_t sc_chunks = (sc_begin - sc_a0 + (uint32_t)nr * (uint32_t)spr * 2u + 15u) >> 4;
     u32x4 sc_first = u32x4{};
     if ((uint32_t)tid < sc_chunks) sc_first = load16_tail(sres, sc_a0 + (uint32_t)tid * 16u, sc_bytes);
-    constexpr int kBatch = 4;
-    for (int p0 = tid; p0 < M * chunks; p0 += kBatch * kThreads) {
-      u32x4 v[kBatch];
+    // thread tid takes chunks c0 + tid and c0 + tid + kThreads of every row: 2 M
+    // loads in flight, no index division
+    for (int c0 = 0; c0 < chunks; c0 += 2 * kThreads) {
+      u32x4 v[2][M];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int p = p0 + j * kThreads;
-        const int m = p / chunks, c = p - (p / chunks) * chunks;
-        const bool ok = p < M * chunks && 8 * c < K;
-        v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            xres, ok ? ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)c) * 2u : kOutOfRange, 0, 0));
+      for (int h = 0; h < 2; ++h) {
+        const int c = c0 + h * kThreads + tid;
+        const bool ok = c < chunks && 8 * c < K;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          v[h][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+              xres, ok ? ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)c) * 2u : kOutOfRange, 0, 0));
       }
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int p = p0 + j * kThreads;
-        const int m = p / chunks, c = p - (p / chunks) * chunks;
-        if (p < M * chunks)
-          *reinterpret_cast<u32x4*>(smem + L.xs + (uint32_t)m * xp + 16u * (uint32_t)c) = permute_a(v[j]);
-        // the 32-k sum over 4 chunks, which are 4 consecutive lanes (one DPP quad;
-        // chunks per row are a multiple of 4 and so is the thread count)
-        const uint32_t one2 = 0x3C003C00u;   // fp16 pair (1, 1)
-        float sum = dot2(v[j].x, one2, 0.f);
-        sum = dot2(v[j].y, one2, sum);
-        sum = dot2(v[j].z, one2, sum);
-        sum = dot2(v[j].w, one2, sum);
-        sum = dpp_add<0xB1>(sum);    // quad_perm [1,0,3,2]
-        sum = dpp_add<0x4E>(sum);    // quad_perm [2,3,0,1]
-        if (p < M * chunks && (c & 3) == 0) reinterpret_cast<float*>(smem + L.xsum)[(c >> 2) * 4 + m] = sum;
+      for (int h = 0; h < 2; ++h) {
+        const int c = c0 + h * kThreads + tid;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          if (c < chunks)
+            *reinterpret_cast<u32x4*>(smem + L.xs + (uint32_t)m * xp + 16u * (uint32_t)c) = permute_a(v[h][m]);
+          // the 32-k sum over 4 chunks, which are 4 consecutive lanes (one DPP quad;
+          // chunks per row are a multiple of 4 and so is the thread count)
+          const uint32_t one2 = 0x3C003C00u;   // fp16 pair (1, 1)
+          float sum = dot2(v[h][m].x, one2, 0.f);
+          sum = dot2(v[h][m].y, one2, sum);
+          sum = dot2(v[h][m].z, one2, sum);
+          sum = dot2(v[h][m].w, one2, sum);
+          sum = dpp_add<0xB1>(sum);    // quad_perm [1,0,3,2]
+          sum = dpp_add<0x4E>(sum);    // quad_perm [2,3,0,1]
+          if (c < chunks && (c & 3) == 0) reinterpret_cast<float*>(smem + L.xsum)[(c >> 2) * 4 + m] = sum;
+        }
       }
     }
     if ((uint32_t)tid < sc_chunks) *reinterpret_cast<u32x4*>(smem + L.sc + (uint32_t)tid * 16u) = sc_first;
@@ -225,7 +232,7 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
     // add the eight chunk lanes of each row: lane bits 2, 3 (DPP), then bit 4
     f32x4 v = acc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < M; ++i) {
       float t = dpp_add<0x124>(v[i]);   // row_ror:4
       t = dpp_add<0x128>(t);            // row_ror:8
       t += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));   // lane ^ 16
@@ -249,13 +256,13 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
     }
     // the lane's chunk is one group; rows past the workgroup's range and chunks
     // past K (zero weights) take scale 0
-    const int kc = KL * s + 32 * lc;
-    const bool ok = lr < nr - kRows * b && kc < K;
+    const uint32_t kc = (uint32_t)(KL * s + 32 * lc);
+    const bool ok = lr < nr - kRows * b && kc < (uint32_t)K;
     const float sc =
-        ok ? half_bits_to_float(*reinterpret_cast<const uint16_t*>(scb + 2 * (kRows * b * spr + kc / G))) : 0.f;
+        ok ? half_bits_to_float(*reinterpret_cast<const uint16_t*>(scb + 2u * ((uint32_t)(kRows * b * spr) + kc / G))) : 0.f;
     const f32x4 xsum = *reinterpret_cast<const f32x4*>(xsa + 128u * (uint32_t)s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, __builtin_fmaf(-1032.f, xsum[i], t[i]), acc[i]);
+    for (int i = 0; i < M; ++i) acc[i] = __builtin_fmaf(sc, __builtin_fmaf(-1032.f, xsum[i], t[i]), acc[i]);
     if (++s == lines) {
       flush();
       s = 0;
