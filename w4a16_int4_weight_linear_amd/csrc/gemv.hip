@@ -421,18 +421,15 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     cur_pos = nxt;
     if constexpr (kReadAhead) cur = on;
   };
-  int base = 0;
-  for (; base + U <= cnt_items; base += U) {
+  // The wave's last items run through the same loop (a wave-uniform test skips
+  // the slots past the end; their loads are out of range and touch no memory),
+  // so no separate straight-line tail is fetched cold while the stream drains.
+  for (int base = 0; base < cnt_items; base += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      consume(u, base + u);
+      if (base + u < cnt_items) consume(u, base + u);
       issue(u);
     }
-  }
-  // The last items of the wave: nothing left to load.
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (base + u < cnt_items) consume(u, base + u);
   }
   // A row cut at the end of the wave's range, then whatever is still queued.
   if (cnt_items > 0 && row < nr && row * C < (t1 << 6)) push_row(acc);
