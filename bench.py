@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--components", default="decode,c1,np4,batch16,swiglu,prefill,moe,moe_ffn,probe",
-                    help="comma list of parts to measure (decode is the headline)")
+                    help="comma list of parts to measure (decode is the headline; without it, a profiling "
+                         "run of the listed parts, which may also name m1 = the M=1 launches alone, and probe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch a 256 MiB elementwise copy and the decode GEMV "
@@ -54,6 +55,12 @@ def parse():
     ap.add_argument("--counter-summary", nargs=3, metavar=("COUNTER_CSV", "OUT_MD", "COMMAND"),
                     help="turn a rocprofv3 --pmc counter_collection.csv into a per-kernel, per-workload "
                          "summary with derived clock, MFMA busy and instructions per MFMA (host only, no GPU)")
+    ap.add_argument("--traffic-table", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "COMMAND"),
+                    help="per-workload HBM read/write bytes of the decode kernels from a FETCH_SIZE and a "
+                         "WRITE_SIZE pass (host only, no GPU)")
+    ap.add_argument("--stream-counter-table", nargs="+", metavar="ARG",
+                    help="OUT_MD COMMAND CSV [CSV ...]: per-workload SQ/TCP counters of the weight-streaming "
+                         "kernels from one or more --pmc passes (host only, no GPU)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "COMMAND"),
                     help="turn a rocprofv3 kernel trace of this benchmark into the per-kernel "
                          "summaries profiles/*.kernel_trace.md (host only, no GPU)")
@@ -573,81 +580,118 @@ def traffic_reduce(fetch_csv, write_csv):
     print(json.dumps(rec))
 
 
+# Workloads of each kernel family as the benchmark runs them (in time order),
+# and the profiles/ file each family's summaries go to.  A list names the
+# workloads of a family in order (one grid each, or split in time); {"by_grid":
+# [...]} gives one such list per grid, smallest grid first.
+TRACE_LABELS = {
+    "gemm_kernel": ["M=512", "M=4096"],
+    "gemv_kernel<1, false>": ["M=1 decode: up 5120->17408 / down 17408->5120 (same bytes)",
+                              "M=1 smoke shape 1x1024x1024"],
+    "gemv_kernel<1, true>": ["M=1, gate+up 5120->2x17408 (SwiGLU)"],
+    "gemv_mfma_kernel<4, 128, false>": ["N=5120", "N=17408"],
+    "gemv_mfma_kernel<4, 128, true>": ["M=4, gate+up 5120->2x17408 (SwiGLU)"],
+    "gemm_skinny_kernel": ["M=16, up 5120->17408 (batched decode)"],
+    "grouped_gemm_kernel<32, true, false>": {"by_grid": [
+        ["256 experts x [512 x 2048] g32, 4096 routed rows, uniform top-8",
+         "same bank, Zipf-skewed top-8 (244 experts used)",
+         "uniform routing, rows gathered by token index (inside the whole MoE layer)",
+         "uniform routing, rows gathered by token index (product alone)"],
+        ["MoE FFN expert down 512->2048 g32, 4096 routed rows (in the layer step, then alone)"]]},
+    "grouped_gemm_kernel<32, true, true>": [
+        "MoE FFN expert gate+up 2048->2x512 g32 with SwiGLU, 4096 routed rows (in the layer step, then alone)"],
+    "stream_read_kernel": ["HBM read probe: launch-sized reads over rotating buffers", "HBM read probe: 1 GiB reads"],
+}
+TRACE_FILES = {
+    "gemv_kernel<1, false>": "gemv_m1_decode_27b_ffn",
+    "gemv_kernel<1, true>": "swiglu_gate_up_27b",
+    "gemv_mfma_kernel<4, 128, false>": "gemv_m4_np4_27b_ffn",
+    "gemv_mfma_kernel<4, 128, true>": "swiglu_gate_up_27b",
+    "gemm_skinny_kernel": "gemm_skinny_m16_27b_up",
+    "gemm_kernel": "gemm_prefill_27b_ffn",
+    "grouped_gemm_kernel<32, true, false>": "grouped_gemm_moe_256e",
+    "grouped_gemm_kernel<32, true, true>": "grouped_gemm_moe_256e",
+    "stream_read_kernel": "hbm_read_probe",
+}
+
+
+def _split_runs(d, n):
+    """Split (start, item) pairs, in time order, into n runs at the n - 1 largest pauses
+    between consecutive starts (the benchmark runs its workloads one after another);
+    every run keeps at least 1/(4 n) of the items."""
+    d = sorted(d, key=lambda t: t[0])
+    if n <= 1 or len(d) < 2:
+        return [[x for _, x in d]]
+    least = max(1, len(d) // (4 * n))
+    cuts = [0, len(d)]
+    for i in sorted(range(1, len(d)), key=lambda i: d[i][0] - d[i - 1][0], reverse=True):
+        if len(cuts) == n + 1:
+            break
+        trial = sorted(cuts + [i])
+        if all(trial[j + 1] - trial[j] >= least for j in range(len(trial) - 1)):
+            cuts = trial
+    return [[x for _, x in d[cuts[i]:cuts[i + 1]]] for i in range(len(cuts) - 1)]
+
+
+def _family(short):
+    return next((b for b in TRACE_FILES if short.startswith(b)), None)
+
+
+def _label_runs(base, items):
+    """[(label, [payload])] for one kernel family; items are (grid, start, payload)."""
+    spec = TRACE_LABELS[base]
+    grids = sorted({g for g, _, _ in items})
+    if isinstance(spec, dict):
+        per_grid = [(g, spec["by_grid"][i] if i < len(spec["by_grid"]) else [f"grid {g}"]) for i, g in enumerate(grids)]
+    elif len(spec) > 1 and len(grids) == len(spec):
+        per_grid = [(g, [lab]) for g, lab in zip(grids, spec)]
+    else:
+        per_grid = [(None, spec)]
+    out = []
+    for g, labs in per_grid:
+        sub = [(t, p) for gg, t, p in items if g is None or gg == g]
+        runs = [[p for _, p in sub]] if len(labs) == 1 else _split_runs(sub, len(labs))
+        out.extend(zip(labs, runs))
+    return out
+
+
 def trace_summary(trace_csv, command):
     """Per-kernel launch statistics of a rocprofv3 kernel trace of bench.py.
 
-    Launches of one kernel with the same grid are split into the benchmark's
-    workloads at the largest gaps between their durations (the workloads of a
-    kernel differ in size: M = 512 / 4096 prefill, N = 5120 / 17408 np4)."""
+    The launches of each kernel family are assigned to the benchmark's workloads
+    by grid and, where workloads share a grid, by time order: the benchmark runs
+    them one after another, so they are split at the largest pauses between
+    consecutive launch starts (TRACE_LABELS)."""
     import csv
     import statistics
     from collections import defaultdict
-    labels = {"gemm_kernel": ["M=512", "M=4096"],
-              "gemv_kernel<1, false>": ["one of up 5120->17408 / down 17408->5120 (same bytes)"],
-              "gemv_kernel<1, true>": ["M=1, gate+up 5120->2x17408 (SwiGLU)"],
-              "gemv_mfma_kernel<4, 128, true, false>": ["N=5120", "N=17408"],
-              "gemv_mfma_kernel<4, 128, true, true>": ["M=4, gate+up 5120->2x17408 (SwiGLU)"],
-              "gemm_skinny_kernel": ["M=16, up 5120->17408 (batched decode)"],
-              "grouped_gemm_kernel": ["256 experts x [512 x 2048] g32, 4096 routed rows, uniform top-8",
-                                      "same bank, Zipf-skewed top-8 (244 experts used)",
-                                      "uniform routing, rows gathered by token index (inside the whole MoE layer)",
-                                      "uniform routing, rows gathered by token index (product alone)"]}
-    files = {"gemv_kernel<1, false>": "gemv_m1_decode_27b_ffn", "gemv_kernel<1, true>": "swiglu_gate_up_27b",
-             "gemv_mfma_kernel<4, 128, true, false>": "gemv_m4_np4_27b_ffn",
-             "gemv_mfma_kernel<4, 128, true, true>": "swiglu_gate_up_27b",
-             "gemm_skinny_kernel": "gemm_skinny_m16_27b_up",
-             "gemm_kernel": "gemm_prefill_27b_ffn", "grouped_gemm_kernel": "grouped_gemm_moe_256e"}
-    groups = defaultdict(list)
+    fams = defaultdict(list)
     with open(trace_csv) as f:
         for r in csv.DictReader(f):
             name = r["Kernel_Name"]
             if "w4a16" not in name:
                 continue
             short = name.replace("w4a16::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-            key = (short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]),
-                   int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]))
-            groups[key].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0))
-
-    def clusters(d, n):
-        # The benchmark runs its workloads one after another: split the launches,
-        # in time order, at the n - 1 largest pauses between consecutive starts.
-        # Each workload is a sizeable run (a warm-up launch alone before a graph
-        # capture pause is not one): every segment keeps >= 1/(4 n) of the launches.
-        d = sorted(d)
-        if n <= 1 or len(d) < 2:
-            return [sorted(t for _, t in d)]
-        least = max(1, len(d) // (4 * n))
-        cuts = [0, len(d)]
-        for i in sorted(range(1, len(d)), key=lambda i: d[i][0] - d[i - 1][0], reverse=True):
-            if len(cuts) == n + 1:
-                break
-            trial = sorted(cuts + [i])
-            if all(trial[j + 1] - trial[j] >= least for j in range(len(trial) - 1)):
-                cuts = trial
-        return [sorted(t for _, t in d[cuts[i]:cuts[i + 1]]) for i in range(len(cuts) - 1)]
-
+            base = _family(short)
+            if base is None:
+                continue
+            shape = (short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]),
+                     int(r["VGPR_Count"]), int(r["Accum_VGPR_Count"]))
+            fams[base].append((shape[1], int(r["Start_Timestamp"]),
+                               (shape, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)))
     out = defaultdict(list)
-    per_base = defaultdict(list)
-    for key in sorted(groups, key=lambda t: (t[0], t[1])):
-        base = next((b for b in files if key[0].startswith(b)), None)
-        if base is not None:
-            per_base[base].append(key)
-    for base, keys in per_base.items():
-        lab = labels[base]
-        # Workloads on distinct grids (one per label, in order of grid size) need no
-        # clustering; workloads sharing a grid are split at the duration gaps.
-        by_grid = len(keys) == len(lab) and len(lab) > 1
-        for j, key in enumerate(keys):
-            k, grid, wg, lds, vgpr, agpr = key
-            d = groups[key]
-            named = [(lab[j], sorted(t for _, t in d))] if by_grid else list(zip(lab, clusters(d, len(lab))))
-            for name, c in named:
-                out[base].append((k, name, grid, wg, lds, vgpr, agpr, len(c), statistics.mean(c),
-                                  statistics.median(c), min(c), max(c)))
+    for base in sorted(fams):
+        for name, run in _label_runs(base, fams[base]):
+            if not run:
+                continue
+            k, grid, wg, lds, vgpr, agpr = run[0][0]
+            c = sorted(t for _, t in run)
+            out[base].append((k, name, grid, wg, lds, vgpr, agpr, len(c), statistics.mean(c),
+                              statistics.median(c), min(c), max(c)))
     # One file per workload family (the SwiGLU pair runs on two kernels).
     by_file = defaultdict(list)
     for base, lst in out.items():
-        by_file[files[base]].append((base, lst))
+        by_file[TRACE_FILES[base]].append((base, lst))
     for fname, parts in by_file.items():
         lst = [row for _, part in parts for row in part]
         path = os.path.join(ROOT, "profiles", f"{fname}.kernel_trace.md")
@@ -663,6 +707,129 @@ def trace_summary(trace_csv, command):
                 f.write(f"| {k} | {name} | {grid} | {wg} | {lds} | {vgpr} | {agpr} | {n} | {mean:.2f} | "
                         f"{med:.2f} | {mn:.2f} | {mx:.2f} |\n")
         print("wrote", path)
+
+
+def _labelled_dispatches(path):
+    """The library's dispatches in one rocprofv3 counter_collection.csv, as
+    {(kernel family, workload label): [dispatch dicts]}; a dispatch dict holds the
+    duration (us) and every counter of the pass.  Workloads of one kernel on
+    distinct grids are told apart by grid; workloads sharing a grid by time order
+    (split at the largest pauses); a family with one label keeps all its launches."""
+    import csv
+    from collections import defaultdict
+    disp = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if "w4a16" not in r["Kernel_Name"]:
+                continue
+            d = disp.setdefault(int(r["Dispatch_Id"]), {
+                "short": r["Kernel_Name"].replace("w4a16::(anonymous namespace)::", "").replace("void ", "").split("(")[0],
+                "grid": int(r["Grid_Size"]), "start": int(r["Start_Timestamp"]),
+                "dur_us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    fams = defaultdict(list)
+    for d in disp.values():
+        base = _family(d["short"])
+        if base is not None:
+            fams[base].append((d["grid"], d["start"], d))
+    return {(base, name): run for base in fams for name, run in _label_runs(base, fams[base]) if run}
+
+
+def _algorithmic_rw(base, label):
+    """(read, write) algorithmic bytes of one launch of a decode workload, or None."""
+    rw = lambda m, n, k, g: (n * k // 2 + n * (k // g) * 2 + m * k * 2, m * n * 2)
+    table = {
+        ("gemv_mfma_kernel<4, 128, false>", "N=5120"): rw(4, 5120, 5120, 128),
+        ("gemv_mfma_kernel<4, 128, false>", "N=17408"): rw(4, 17408, 5120, 128),
+        ("gemv_kernel<1, true>", "M=1, gate+up 5120->2x17408 (SwiGLU)"): rw(1, 2 * 17408, 5120, 128),
+        ("gemv_mfma_kernel<4, 128, true>", "M=4, gate+up 5120->2x17408 (SwiGLU)"): rw(4, 2 * 17408, 5120, 128),
+    }
+    r = table.get((base, label))
+    if r is not None and "SwiGLU" in label:
+        r = (r[0], r[1] // 2)        # one output per gate/up pair
+    return r
+
+
+def traffic_table(fetch_csv, write_csv, out_md, command):
+    """HBM bytes per launch of each decode workload from a FETCH_SIZE and a WRITE_SIZE
+    pass: medians over each workload's dispatches, scaled by the factors a plain
+    256 MiB copy gives (profiles/gemv.traffic.json, written by --traffic-reduce)."""
+    import statistics
+    with open(os.path.join(ROOT, "profiles", "gemv.traffic.json")) as f:
+        sc = json.load(f)
+    fs, ws = sc["fetch_scale"], sc["write_scale"]
+    fe, wr = _labelled_dispatches(fetch_csv), _labelled_dispatches(write_csv)
+    lines = ["| kernel | workload | dispatches | HBM read MB | HBM write MB | algorithmic read MB | "
+             "algorithmic write MB |", "|---|---|---|---|---|---|---|"]
+    for key in sorted(fe):
+        if key not in wr:
+            continue
+        rd = statistics.median(d["FETCH_SIZE"] for d in fe[key]) * 1024 * fs / 1e6
+        wt = statistics.median(d["WRITE_SIZE"] for d in wr[key]) * 1024 * ws / 1e6
+        algo = _algorithmic_rw(*key)
+        a_r, a_w = (f"{algo[0] / 1e6:.2f}", f"{algo[1] / 1e6:.3f}") if algo else ("", "")
+        lines.append(f"| {key[0]} | {key[1]} | {len(fe[key])} | {rd:.2f} | {wt:.3f} | {a_r} | {a_w} |")
+    with open(out_md, "w") as f:
+        f.write("Commands (from the repository root on the GPU box), then the summary:\n\n```\n"
+                f"{command}\npython3 bench.py --traffic-table <fetch dir>/p_counter_collection.csv "
+                f"<write dir>/p_counter_collection.csv {out_md} '<commands>'\n```\n\n"
+                f"FETCH_SIZE x {fs} and WRITE_SIZE x {ws}: the factors a plain 256 MiB elementwise copy gives "
+                "on this part (profiles/gemv.traffic.json). Medians over each workload's dispatches; "
+                "MB = 10^6 bytes.\n\n")
+        f.write("\n".join(lines) + "\n")
+    print("wrote", out_md)
+
+
+def stream_counter_table(csv_paths, out_md, command):
+    """Per-workload SQ/TCP counters of weight-streaming kernels from one or more --pmc
+    passes over the same benchmark command (each pass is its own run; counters are
+    averaged per workload and the passes joined by workload).
+
+    Per-wave figures divide the summed counters by SQ_WAVES; the wave-cycle
+    fractions are each counter over SQ_WAVE_CYCLES (both summed over waves):
+    active = issuing any instruction, VALU = issuing VALU, wait = waiting on a
+    dependency counter (s_waitcnt), issue-stall = ready but not picked.  The L1 to
+    L2 read latency is TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles)."""
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(list))
+    for p in csv_paths:
+        for key, ds in _labelled_dispatches(p).items():
+            for d in ds:
+                for c, v in d.items():
+                    if isinstance(v, float) and c != "start":
+                        acc[key][c].append(float(v))
+    mean = lambda key, c: (sum(acc[key][c]) / len(acc[key][c])) if acc[key].get(c) else None
+    cols = [("dispatches", lambda k: str(len(acc[k]["dur_us"]))),
+            ("mean us", lambda k: f"{mean(k, 'dur_us'):.2f}")]
+    per_wave = [("VALU", "SQ_INSTS_VALU"), ("SALU", "SQ_INSTS_SALU"), ("LDS", "SQ_INSTS_LDS"),
+                ("MFMA", "SQ_INSTS_MFMA"), ("VMEM rd", "SQ_INSTS_VMEM_RD")]
+    frac = [("active", "SQ_ACTIVE_INST_ANY"), ("VALU busy", "SQ_ACTIVE_INST_VALU"), ("wait", "SQ_WAIT_ANY"),
+            ("issue-stall", "SQ_WAIT_INST_ANY")]
+
+    def fmt(v, spec):
+        return "" if v is None else format(v, spec)
+    for name, c in per_wave:
+        cols.append((f"{name} / wave", lambda k, c=c: fmt(mean(k, c) / mean(k, "SQ_WAVES")
+                                                          if mean(k, c) is not None and mean(k, "SQ_WAVES") else None, ".0f")))
+    for name, c in frac:
+        cols.append((f"{name} (of wave cycles)", lambda k, c=c: fmt(mean(k, c) / mean(k, "SQ_WAVE_CYCLES")
+                                                                    if mean(k, c) is not None and mean(k, "SQ_WAVE_CYCLES") else None, ".3f")))
+    cols.append(("L1->L2 read latency (cycles)",
+                 lambda k: fmt(mean(k, "TCP_TCC_READ_REQ_LATENCY") / mean(k, "TCP_TCC_READ_REQ")
+                               if mean(k, "TCP_TCC_READ_REQ") else None, ".0f")))
+    lines = ["| kernel | workload | " + " | ".join(n for n, _ in cols) + " |",
+             "|---|---|" + "---|" * len(cols)]
+    for key in sorted(acc):
+        lines.append(f"| {key[0]} | {key[1]} | " + " | ".join(fn(key) for _, fn in cols) + " |")
+    with open(out_md, "w") as f:
+        f.write("Commands (from the repository root on the GPU box), then the summary:\n\n```\n"
+                f"{command}\npython3 bench.py --stream-counter-table {out_md} '<commands>' <pass csv> ...\n```\n\n"
+                "Per-wave counts are summed counters over SQ_WAVES; fractions are of SQ_WAVE_CYCLES "
+                "(both summed over waves): active = issuing, VALU busy = issuing VALU, wait = held by "
+                "s_waitcnt, issue-stall = ready but not picked.  Durations are the profiled (eager, "
+                "serialised) dispatches, not graph replays.\n\n")
+        f.write("\n".join(lines) + "\n")
+    print("wrote", out_md)
 
 
 XCDS = 8   # MI355X: GRBM counters are reported once per XCD and summed by the profiler
@@ -886,6 +1053,13 @@ def main():
     if args.counter_summary:
         counter_summary(*args.counter_summary)
         return
+    if args.traffic_table:
+        traffic_table(*args.traffic_table)
+        return
+    if args.stream_counter_table:
+        out_md, command, *csvs = args.stream_counter_table
+        stream_counter_table(csvs, out_md, command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1",
                           "reason": "the W4A16 layer is built and measured on a single MI355X"}))
@@ -903,7 +1077,13 @@ def main():
     comps = [c for c in args.components.split(",") if c]
     res = {}
     if "decode" not in comps:
-        # component runs without the headline (profiling passes): no JSON line contract
+        # component runs without the headline (profiling passes): no JSON line contract.
+        # The parts run in the same order as in the full benchmark, so profiles of
+        # either kind assign launches to workloads the same way.
+        if "m1" in comps:
+            # the M = 1 decode launches alone (up and down projections)
+            d = decode_component(torch, w4, synth, args)
+            res["m1"] = {k: d[k] for k in ("ms_per_step", "step_bytes", "gbs", "kernel")}
         for name, fn in (("c1", c1_component), ("np4", np4_component), ("batch16", batched_decode_component),
                          ("swiglu", swiglu_component), ("prefill", prefill_component), ("moe", moe_component),
                          ("moe_ffn", moe_ffn_component)):
@@ -911,6 +1091,8 @@ def main():
                 res[name] = fn(torch, w4, synth, args)
         if "dense_ref" in comps:
             res["dense_ref"] = dense_fp16_reference(torch)
+        if "probe" in comps:
+            res["probe"] = hbm_read_probe(torch, w4, dense_bytes(1, 17408, 5120, 128), args.steps)
         print(json.dumps({"components": res}, default=float))
         return
     decode = decode_component(torch, w4, synth, args)
