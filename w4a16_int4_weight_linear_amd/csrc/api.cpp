@@ -89,13 +89,20 @@ w4a16_status as_status(int s) { return static_cast<w4a16_status>(s); }
 // (m <= 4: the decode GEMV kernels while their plan fits; 5..32: the
 // weight-streaming MFMA kernel, one pass per 16 rows); otherwise the tiled GEMM,
 // the only one that uses the workspace.
+// Fewest activation rows that the decode GEMV runs on the MFMA kernel (below: the
+// per-lane dot-product kernel).
+#ifndef W4A16_MFMA_MIN_ROWS
+#define W4A16_MFMA_MIN_ROWS 2
+#endif
+constexpr int64_t kMfmaMinRows = W4A16_MFMA_MIN_ROWS;
+
 enum class GemmPath { kGemv, kSkinny, kTiled };
 
 GemmPath gemm_path(int64_t m, int64_t n, int64_t k, int32_t group, const DeviceInfo& dev) {
   if (m <= 4) {
     int mb = 0;
     size_t mlds = 0;
-    if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, group, dev, &mb, &mlds)) return GemmPath::kGemv;
+    if (m >= kMfmaMinRows && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, group, dev, &mb, &mlds)) return GemmPath::kGemv;
     if (w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev).ok) return GemmPath::kGemv;
   }
   if (m <= 32 && w4a16::gemm_skinny_fits((int)(m < 16 ? m : 16), (int)n, (int)k, dev)) return GemmPath::kSkinny;
@@ -118,11 +125,11 @@ int skinny_passes(const uint16_t* x, const uint32_t* packed, const uint16_t* sca
 // Returns -1 when no GEMV plan fits this k (the activations do not fit in LDS).
 int gemv_dispatch(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int64_t m,
                   int64_t n, int64_t k, int32_t group, const DeviceInfo& dev, hipStream_t st) {
-  // Three or four activation rows: the MFMA kernel (faster there; at two rows the
-  // per-lane kernel is), while its activations fit in LDS.
+  // Two to four activation rows: the MFMA kernel (faster there; measured 12% at two
+  // rows), while its activations fit in LDS; else the per-lane kernel.
   int mb = 0;
   size_t mlds = 0;
-  if (m >= 3 && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, group, dev, &mb, &mlds))
+  if (m >= kMfmaMinRows && w4a16::gemv_mfma_plan((int)m, (int)n, (int)k, group, dev, &mb, &mlds))
     return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)n, (int)k, group, mb, mlds, dev, st));
   const w4a16::GemvPlan plan = w4a16::gemv_plan((int)m, (int)n, (int)k, group, dev);
   if (!plan.ok) return -1;
@@ -270,11 +277,11 @@ w4a16_status w4a16_gemv_swiglu(const uint16_t* x, const uint32_t* packed, const 
   if (w4a16::current_device_info(&dev) != hipSuccess) return W4A16_ERR_HIP;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (k == 0) return status_of(w4a16::launch_zero_fill(y, (size_t)(m * n), st));   // SiLU(0) * 0
-  // Up to four rows: the decode GEMV kernels with the gate/up epilogue (three or
+  // Up to four rows: the decode GEMV kernels with the gate/up epilogue (two to
   // four rows on MFMA, as for the plain product), while the activations fit in LDS.
   int mb = 0;
   size_t mlds = 0;
-  if (m >= 3 && m <= 4 && w4a16::gemv_mfma_plan((int)m, (int)(2 * n), (int)k, group, dev, &mb, &mlds, true))
+  if (m >= kMfmaMinRows && m <= 4 && w4a16::gemv_mfma_plan((int)m, (int)(2 * n), (int)k, group, dev, &mb, &mlds, true))
     return status_of(w4a16::launch_gemv_mfma(x, packed, scales, y, (int)m, (int)(2 * n), (int)k, group, mb, mlds,
                                              dev, st, true));
   if (m <= 4) {
