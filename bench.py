@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--components", default="decode,c1,np4,batch16,swiglu,prefill,moe,moe_ffn,probe",
+    ap.add_argument("--components", default="decode,c1,np4,batch16,swiglu,prefill,moe,moe_ffn,shard,probe",
                     help="comma list of parts to measure (decode is the headline; without it, a profiling "
                          "run of the listed parts, which may also name m1 = the M=1 launches alone, and probe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -449,6 +449,64 @@ def moe_component(torch, w4, synth, args):
             "layer_route_gather_combine": {"ms": mean3, "tokens": c.tokens}}
 
 
+def shard_component(torch, w4, synth, args, parts=8):
+    """Not graded: one GPU's share of the 27B FFN and of the MoE bank when the layer is
+    split over `parts` GPUs (design only; nothing here exchanges data between GPUs):
+    the column-parallel up projection (its first N/parts rows: 5120 -> 2176), the
+    row-parallel down projection (its first K/parts columns: 2176 -> 5120, whose partial
+    sums an all-reduce would add) and the expert-parallel grouped product (experts
+    0 .. E/parts - 1 with the rows routed to them)."""
+    out = {}
+    up = synth.DENSE_CASES["gemv_up_1x5120x17408_g128"]
+    down = synth.DENSE_CASES["gemv_down_1x17408x5120_g128"]
+    wu, xu = synth.dense_inputs(up)
+    wd, xd = synth.dense_inputs(down)
+    nu, kd = up.n // parts, down.k // parts
+    shapes = {f"gemv_up_shard_1x{up.k}x{nu}_g128": (wu[:nu], xu),
+              f"gemv_down_shard_1x{kd}x{down.n}_g128": (np.ascontiguousarray(wd[:, :kd]), np.ascontiguousarray(xd[:, :kd]))}
+    del wu, wd
+    for name, (w, x) in shapes.items():
+        p, sc = w4.quantize(w, 128)
+        pool = make_pool(torch, p, sc)
+        xt = torch.from_numpy(x).to("cuda")
+        y = torch.empty((1, w.shape[0]), dtype=torch.float16, device="cuda")
+
+        def one(i):
+            pp, ss = pool[i % len(pool)]
+            w4.gemv(xt, pp, ss, 128, out=y)
+
+        t = per_launch(torch, one, args.steps, graph=True, outputs=(y,))
+        b = dense_bytes(1, w.shape[0], w.shape[1], 128)
+        out[name] = {"bytes": b, **timing_fields(t, b, 1e9, "gbs")}
+        out[name]["hbm_frac"] = out[name]["gbs"] / HBM_PEAK_GBS
+        del pool
+    c = synth.MOE_CASES["moe_256e_512x2048_g32_top8"]
+    ws, x, r = synth.moe_inputs(c)
+    ex = c.experts // parts
+    packed = np.empty((ex, c.n, c.k // 8), np.uint32)
+    scales = np.empty((ex, c.n, c.k // c.group), np.float16)
+    for e in range(ex):
+        packed[e], scales[e] = w4.quantize(ws[e], c.group)
+    del ws
+    rows = int(r.offsets[ex])                   # pairs are sorted by expert: the first experts' rows lead
+    pool = make_pool(torch, packed, scales)
+    xs = torch.from_numpy(x[r.pair_token[:rows]]).to("cuda")
+    offs = torch.from_numpy(np.ascontiguousarray(r.offsets[: ex + 1])).to("cuda")
+    y = torch.empty((rows, c.n), dtype=torch.float16, device="cuda")
+
+    def one_moe(i):
+        pp, ss = pool[i % len(pool)]
+        w4.grouped_gemm(xs, pp, ss, offs, c.group, out=y)
+
+    t = per_launch(torch, one_moe, args.steps, graph=True, outputs=(y,))
+    b = ex * c.n * c.k // 2 + ex * c.n * (c.k // c.group) * 2 + rows * c.k * 2 + rows * c.n * 2 + (ex + 1) * 4
+    name = f"moe_shard_{ex}e_{c.n}x{c.k}_g{c.group}"
+    out[name] = {"bytes": b, "rows": rows, **timing_fields(t, b, 1e9, "gbs")}
+    out[name]["hbm_frac"] = out[name]["gbs"] / HBM_PEAK_GBS
+    out["parts"] = parts
+    return out
+
+
 def moe_ffn_component(torch, w4, synth, args):
     """The routed experts' whole FFN at the 35B-A3B-like shape (256 experts, hidden 2048,
     intermediate 512, g32, 512 tokens top-8): route, gathered gate/up + SwiGLU, down
@@ -583,16 +641,19 @@ def traffic_reduce(fetch_csv, write_csv):
 # Workloads of each kernel family as the benchmark runs them (in time order),
 # and the profiles/ file each family's summaries go to.  A list names the
 # workloads of a family in order (one grid each, or split in time); {"by_grid":
-# [...]} gives one such list per grid, smallest grid first.
+# [...]} gives one such list per grid, smallest grid first.  A profiling run of a
+# family must run all of the family's workloads (the default components do).
 TRACE_LABELS = {
     "gemm_kernel": ["M=512", "M=4096"],
     "gemv_kernel<1, false>": ["M=1 decode: up 5120->17408 / down 17408->5120 (same bytes)",
-                              "M=1 smoke shape 1x1024x1024"],
+                              "M=1 smoke shape 1x1024x1024",
+                              "M=1 one GPU's shard of 8: up 5120->2176 / down 2176->5120 (same bytes)"],
     "gemv_kernel<1, true>": ["M=1, gate+up 5120->2x17408 (SwiGLU)"],
     "gemv_mfma_kernel<4, 128, false>": ["N=5120", "N=17408"],
     "gemv_mfma_kernel<4, 128, true>": ["M=4, gate+up 5120->2x17408 (SwiGLU)"],
     "gemm_skinny_kernel": ["M=16, up 5120->17408 (batched decode)"],
     "grouped_gemm_kernel<32, true, false>": {"by_grid": [
+        ["one GPU's shard of 8: experts 0-31 of the bank with the rows routed to them"],
         ["256 experts x [512 x 2048] g32, 4096 routed rows, uniform top-8",
          "same bank, Zipf-skewed top-8 (244 experts used)",
          "uniform routing, rows gathered by token index (inside the whole MoE layer)",
@@ -1086,7 +1147,7 @@ def main():
             res["m1"] = {k: d[k] for k in ("ms_per_step", "step_bytes", "gbs", "kernel")}
         for name, fn in (("c1", c1_component), ("np4", np4_component), ("batch16", batched_decode_component),
                          ("swiglu", swiglu_component), ("prefill", prefill_component), ("moe", moe_component),
-                         ("moe_ffn", moe_ffn_component)):
+                         ("moe_ffn", moe_ffn_component), ("shard", shard_component)):
             if name in comps:
                 res[name] = fn(torch, w4, synth, args)
         if "dense_ref" in comps:
@@ -1110,6 +1171,8 @@ def main():
         res["moe"] = moe_component(torch, w4, synth, args)
     if "moe_ffn" in comps:
         res["moe_ffn"] = moe_ffn_component(torch, w4, synth, args)
+    if "shard" in comps:
+        res["shard_p8"] = shard_component(torch, w4, synth, args)
 
     k = decode["kernel"]
     traffic = traffic_from_profile("gemv", source_hash("gemv.hip", "device.hpp"))
