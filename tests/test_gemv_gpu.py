@@ -149,7 +149,7 @@ def _offset_scales(s: np.ndarray):
     return view
 
 
-@pytest.mark.parametrize("m", [1, 3, 4, 9, 200])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 9, 200])
 @pytest.mark.parametrize("k,group", [(2048, 32), (2304, 128), (5120, 128)])
 def test_scales_at_two_byte_offset(w4, m, k, group):
     """Scales need only 2-byte alignment: a scale pointer 2 bytes past a 16-byte

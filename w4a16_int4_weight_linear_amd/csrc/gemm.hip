@@ -90,7 +90,10 @@ struct GemmPlan {
   int wgs, rounds, sk_tiles, nsk;           // nsk: stream-K workgroups per XCD
 };
 
-constexpr int kMinSKSteps = 2;
+#ifndef W4A16_GEMM_MIN_SK_STEPS
+#define W4A16_GEMM_MIN_SK_STEPS 2
+#endif
+constexpr int kMinSKSteps = W4A16_GEMM_MIN_SK_STEPS;   // K steps per stream-K workgroup, at least
 constexpr int kGroupM = 4;                  // tile rows per group of the tile order
 
 GemmPlan gemm_plan(int m, int n, int k, const DeviceInfo& dev) {
