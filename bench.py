@@ -52,9 +52,10 @@ def parse():
     ap.add_argument("--traffic-reduce", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the two counter_collection.csv files of the --traffic-probe "
                          "passes into profiles/gemv.traffic.json (host only, no GPU)")
-    ap.add_argument("--counter-summary", nargs=3, metavar=("COUNTER_CSV", "OUT_MD", "COMMAND"),
-                    help="turn a rocprofv3 --pmc counter_collection.csv into a per-kernel, per-workload "
-                         "summary with derived clock, MFMA busy and instructions per MFMA (host only, no GPU)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
+                    help="OUT_MD COMMAND CSV [CSV ...]: per-workload counters of the prefill GEMM from one or "
+                         "more --pmc passes, with derived clock, MFMA busy, VALU-MFMA co-execution, VALU issue, "
+                         "LDS read bandwidth and instructions per MFMA (host only, no GPU)")
     ap.add_argument("--traffic-table", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "COMMAND"),
                     help="per-workload HBM read/write bytes of the decode kernels from a FETCH_SIZE and a "
                          "WRITE_SIZE pass (host only, no GPU)")
@@ -896,42 +897,68 @@ def stream_counter_table(csv_paths, out_md, command):
 XCDS = 8   # MI355X: GRBM counters are reported once per XCD and summed by the profiler
 
 
-def counter_summary(csv_path, out_md, command):
-    """Per-kernel counters of one --pmc pass, split into workloads by the MFMA count.
+def counter_summary(csv_paths, out_md, command):
+    """Per-workload counters of the prefill GEMM (and of any other MFMA kernel) from one
+    or more --pmc passes over the same command, joined by workload (TRACE_LABELS).
 
-    Derived: clock = GRBM_GUI_ACTIVE / XCDS / duration (the profiler sums the counter
-    over the XCDs); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GUI cycles per XCD);
+    Derived, where the pass has the counters: clock = GRBM_GUI_ACTIVE / XCDS / duration
+    (the profiler sums the counter over the XCDs); MFMA busy and VALU-MFMA co-execution =
+    SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES over SIMDs x cycles; VALU
+    issue = SQ_ACTIVE_INST_VALU x 4 (quad cycles) over SIMDs x cycles; LDS read bytes per
+    CU and cycle = SQ_INSTS_LDS_LOAD_BANDWIDTH x 64 (64-byte units) over CUs x cycles;
     VALU and LDS instructions per MFMA instruction."""
-    import collections
+    from collections import defaultdict
     import csv
-    disp = collections.defaultdict(dict)
-    for r in csv.DictReader(open(csv_path)):
-        d = disp[int(r["Dispatch_Id"])]
-        d["kernel"] = r["Kernel_Name"]
-        d["grid"] = r["Grid_Size"]
-        d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        d[r["Counter_Name"]] = float(r["Counter_Value"])
-    groups = collections.defaultdict(list)
-    for d in disp.values():
-        if d.get("SQ_INSTS_MFMA", 0) <= 0:
+    acc = defaultdict(lambda: defaultdict(list))
+    for p in csv_paths:
+        for key, ds in _labelled_dispatches(p).items():
+            for d in ds:
+                for c, v in d.items():
+                    if isinstance(v, float) and c != "start":
+                        acc[key][c].append(float(v))
+        # the vendor's dense fp16 GEMM kernels of the same run (bench component dense_ref),
+        # one kernel per shape
+        lib = defaultdict(dict)
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Kernel_Name"].startswith("Cijk_"):
+                    d = lib[int(r["Dispatch_Id"])]
+                    d["name"] = r["Kernel_Name"].split("_SN")[0][:60]
+                    d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    d[r["Counter_Name"]] = float(r["Counter_Value"])
+        for d in lib.values():
+            for c, v in d.items():
+                if c != "name":
+                    acc[("vendor dense fp16 GEMM", d["name"])][c].append(float(v))
+    cus, simds = 256, 4 * 256
+    mean = lambda key, c: (sum(acc[key][c]) / len(acc[key][c])) if acc[key].get(c) else None
+
+    def ratio(key, num, den_fn, scale=1.0, spec=".3f"):
+        v, d = mean(key, num), den_fn(key)
+        return "" if v is None or not d else format(v * scale / d, spec)
+    cycles = lambda k: mean(k, "GRBM_GUI_ACTIVE") / XCDS if mean(k, "GRBM_GUI_ACTIVE") else None
+    cols = [("dispatches", lambda k: str(len(acc[k]["dur_us"]))),
+            ("mean us", lambda k: f"{mean(k, 'dur_us'):.1f}"),
+            ("clock GHz", lambda k: "" if not cycles(k) else f"{cycles(k) / mean(k, 'dur_us') / 1e3:.2f}"),
+            ("MFMA busy", lambda k: ratio(k, "SQ_VALU_MFMA_BUSY_CYCLES", lambda kk: simds * cycles(kk) if cycles(kk) else None)),
+            ("VALU-MFMA co-exec", lambda k: ratio(k, "SQ_VALU_MFMA_COEXEC_CYCLES",
+                                                   lambda kk: simds * cycles(kk) if cycles(kk) else None)),
+            ("VALU issue", lambda k: ratio(k, "SQ_ACTIVE_INST_VALU", lambda kk: simds * cycles(kk) if cycles(kk) else None, 4.0)),
+            ("LDS read B/clk/CU", lambda k: ratio(k, "SQ_INSTS_LDS_LOAD_BANDWIDTH",
+                                                   lambda kk: cus * cycles(kk) if cycles(kk) else None, 64.0, ".1f")),
+            ("VALU/MFMA", lambda k: ratio(k, "SQ_INSTS_VALU", lambda kk: mean(kk, "SQ_INSTS_MFMA"), 1.0, ".2f")),
+            ("LDS/MFMA", lambda k: ratio(k, "SQ_INSTS_LDS", lambda kk: mean(kk, "SQ_INSTS_MFMA"), 1.0, ".2f"))]
+    lines = ["| kernel | workload | " + " | ".join(n for n, _ in cols) + " |", "|---|---|" + "---|" * len(cols)]
+    for key in sorted(acc):
+        if key[0] not in ("gemm_kernel", "vendor dense fp16 GEMM"):
             continue
-        groups[(d["kernel"], d["grid"], round(d["SQ_INSTS_MFMA"], -4))].append(d)
-    simds = 4 * 256
-    lines = ["| kernel | grid | dispatches | mean us | MFMA instr | VALU instr | LDS instr | VALU/MFMA | "
-             "LDS/MFMA | clock GHz | MFMA busy |", "|---|---|---|---|---|---|---|---|---|---|---|"]
-    for (k, g, _), ds in sorted(groups.items(), key=lambda t: t[0][2]):
-        avg = lambda c: sum(d.get(c, 0.0) for d in ds) / len(ds)
-        gui = avg("GRBM_GUI_ACTIVE") / XCDS
-        dur = avg("dur_us")
-        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES") / (simds * gui) if gui else float("nan")
-        name = k.replace("(anonymous namespace)::", "").replace("void ", "", 1).split("(")[0][:70]
-        lines.append(f"| {name} | {g} | {len(ds)} | {dur:.1f} | {avg('SQ_INSTS_MFMA'):.4g} | "
-                     f"{avg('SQ_INSTS_VALU'):.4g} | {avg('SQ_INSTS_LDS'):.4g} | "
-                     f"{avg('SQ_INSTS_VALU') / avg('SQ_INSTS_MFMA'):.2f} | {avg('SQ_INSTS_LDS') / avg('SQ_INSTS_MFMA'):.2f} | "
-                     f"{gui / dur / 1e3:.2f} | {busy:.3f} |")
+        lines.append(f"| {key[0]} | {key[1]} | " + " | ".join(fn(key) for _, fn in cols) + " |")
     with open(out_md, "w") as f:
-        f.write("Command (from the repository root on the GPU box), then the summary:\n\n```\n"
-                f"{command}\npython3 bench.py --counter-summary <pmc dir>/pmc_counter_collection.csv {out_md} '<command>'\n```\n\n")
+        f.write("Commands (from the repository root on the GPU box), then the summary:\n\n```\n"
+                f"{command}\npython3 bench.py --counter-summary {out_md} '<commands>' <pass csv> ...\n```\n\n"
+                "Fractions are of SIMD cycles at the measured clock (GRBM_GUI_ACTIVE per XCD over the "
+                "profiled duration).  LDS read bytes per CU and cycle against the part's ~128 B/clk "
+                "(conflict-free ds_read_b128 reach 114-136 B per CU cycle on this part).\n\n")
         f.write("\n".join(lines) + "\n")
     print("wrote", out_md)
 
@@ -1112,7 +1139,8 @@ def main():
         trace_summary(*args.trace_summary)
         return
     if args.counter_summary:
-        counter_summary(*args.counter_summary)
+        out_md, command, *csvs = args.counter_summary
+        counter_summary(csvs, out_md, command)
         return
     if args.traffic_table:
         traffic_table(*args.traffic_table)
