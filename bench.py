@@ -854,14 +854,16 @@ def stream_counter_table(csv_paths, out_md, command):
     L2 read latency is TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles)."""
     from collections import defaultdict
     acc = defaultdict(lambda: defaultdict(list))
+    passes = defaultdict(int)                   # passes that saw each workload
     for p in csv_paths:
         for key, ds in _labelled_dispatches(p).items():
+            passes[key] += 1
             for d in ds:
                 for c, v in d.items():
                     if isinstance(v, float) and c != "start":
                         acc[key][c].append(float(v))
     mean = lambda key, c: (sum(acc[key][c]) / len(acc[key][c])) if acc[key].get(c) else None
-    cols = [("dispatches", lambda k: str(len(acc[k]["dur_us"]))),
+    cols = [("dispatches per pass", lambda k: str(len(acc[k]["dur_us"]) // max(1, passes[k]))),
             ("mean us", lambda k: f"{mean(k, 'dur_us'):.2f}")]
     per_wave = [("VALU", "SQ_INSTS_VALU"), ("SALU", "SQ_INSTS_SALU"), ("LDS", "SQ_INSTS_LDS"),
                 ("MFMA", "SQ_INSTS_MFMA"), ("VMEM rd", "SQ_INSTS_VMEM_RD")]
@@ -910,8 +912,10 @@ def counter_summary(csv_paths, out_md, command):
     from collections import defaultdict
     import csv
     acc = defaultdict(lambda: defaultdict(list))
+    passes = defaultdict(int)                   # passes that saw each workload
     for p in csv_paths:
         for key, ds in _labelled_dispatches(p).items():
+            passes[key] += 1
             for d in ds:
                 for c, v in d.items():
                     if isinstance(v, float) and c != "start":
@@ -926,6 +930,8 @@ def counter_summary(csv_paths, out_md, command):
                     d["name"] = r["Kernel_Name"].split("_SN")[0][:60]
                     d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                     d[r["Counter_Name"]] = float(r["Counter_Value"])
+        for name in {d["name"] for d in lib.values()}:
+            passes[("vendor dense fp16 GEMM", name)] += 1
         for d in lib.values():
             for c, v in d.items():
                 if c != "name":
@@ -937,7 +943,7 @@ def counter_summary(csv_paths, out_md, command):
         v, d = mean(key, num), den_fn(key)
         return "" if v is None or not d else format(v * scale / d, spec)
     cycles = lambda k: mean(k, "GRBM_GUI_ACTIVE") / XCDS if mean(k, "GRBM_GUI_ACTIVE") else None
-    cols = [("dispatches", lambda k: str(len(acc[k]["dur_us"]))),
+    cols = [("dispatches per pass", lambda k: str(len(acc[k]["dur_us"]) // max(1, passes[k]))),
             ("mean us", lambda k: f"{mean(k, 'dur_us'):.1f}"),
             ("clock GHz", lambda k: "" if not cycles(k) else f"{cycles(k) / mean(k, 'dur_us') / 1e3:.2f}"),
             ("MFMA busy", lambda k: ratio(k, "SQ_VALU_MFMA_BUSY_CYCLES", lambda kk: simds * cycles(kk) if cycles(kk) else None)),
