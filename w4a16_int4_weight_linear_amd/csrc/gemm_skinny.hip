@@ -4,7 +4,7 @@
 // caller makes one pass per 16 rows) is still a pass over the weights: at M = 16 and 4-bit weights there are 8 FLOP per weight
 // byte, far below the MFMA/HBM ridge.  The 128 x 256 tiles of the prefill GEMM
 // compute mostly padding there and spread only N / 256 tiles over the CUs, so
-// this kernel streams the weights like the batched-decode GEMV (gemv_mfma.hip):
+// this kernel streams the weights once, one workgroup per CU:
 //
 // * Each workgroup (one per CU) owns a contiguous range of weight rows (sizes
 //   differ by at most one row), covered by 16-row blocks.  A unit of work is
