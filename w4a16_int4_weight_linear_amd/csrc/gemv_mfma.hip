@@ -60,12 +60,22 @@ namespace {
 #ifndef W4A16_NP4_LOADS_IN_FLIGHT
 #define W4A16_NP4_LOADS_IN_FLIGHT 4
 #endif
+#ifndef W4A16_NP4_SHALLOW_LOADS
+#define W4A16_NP4_SHALLOW_LOADS 3
+#endif
+#ifndef W4A16_NP4_SHALLOW_UNITS
+#define W4A16_NP4_SHALLOW_UNITS 10
+#endif
 #ifndef W4A16_NP4_WG_PER_CU
 #define W4A16_NP4_WG_PER_CU 1
 #endif
 constexpr int kThreads = W4A16_NP4_THREADS;
 constexpr int kWaves = kThreads / 64;
-constexpr int kDepth = W4A16_NP4_LOADS_IN_FLIGHT;   // loads in flight per wave
+// Loads in flight per wave: a wave with few units (a small launch) does better
+// with a shallower ring, a long stream with a deeper one (measured).
+constexpr int kDepth = W4A16_NP4_LOADS_IN_FLIGHT;
+constexpr int kShallowDepth = W4A16_NP4_SHALLOW_LOADS;
+constexpr int kShallowUnits = W4A16_NP4_SHALLOW_UNITS;   // units per wave at or below which it is used
 constexpr int KL = 256;                         // k per line: 128 bytes of a weight row
 constexpr int kRows = 8;                        // weight rows per block (one load)
 constexpr int kMaxBlocks = 32;                  // blocks per workgroup
@@ -108,7 +118,7 @@ __device__ inline f16x4 as_h4(uint32_t a, uint32_t b) { return __builtin_bit_cas
 // rows_base / rows_extra count row units: single rows, or (gate, up) row pairs
 // (GATED).  `scales` is rounded down to 16 bytes by the launcher and sc_shift
 // bytes added back here, so the 16-byte staging loads are aligned in memory.
-template <int M, int G, bool GATED>
+template <int M, int G, bool GATED, int D>
 __global__ void __launch_bounds__(kThreads)
 gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
                  const uint16_t* __restrict__ scales, uint16_t* __restrict__ y,
@@ -145,7 +155,7 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   // cursors (wave-uniform): the next unit to load is (ib, is), line-minor
   const int b_first = u0 / lines, s_first = u0 - b_first * lines;
   int iu = u0, ib = b_first, is = s_first;
-  u32x4 ring[kDepth];
+  u32x4 ring[D];
   // Every slot is loaded unconditionally, in a fixed order, so the compiler can
   // wait for each load alone (vmcnt); a load past the wave's units has an
   // out-of-range offset and a zero scalar offset: it touches no memory.
@@ -161,7 +171,7 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
     }
   };
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) issue(d);
+  for (int d = 0; d < D; ++d) issue(d);
 
   // ---- stage the activations (and their 32-k sums), the scales, zero partials ----
   {
@@ -270,15 +280,15 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
     }
   };
   int u = u0;
-  for (; u + kDepth <= u1; u += kDepth) {
+  for (; u + D <= u1; u += D) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
+    for (int d = 0; d < D; ++d) {
       consume(ring[d]);
       issue(d);
     }
   }
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
+  for (int d = 0; d < D; ++d)
     if (u + d < u1) consume(ring[d]);
   if (s != 0) flush();
 
@@ -315,12 +325,12 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   }
 }
 
-template <int M, int G, bool GATED>
-hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
+template <int M, int G, bool GATED, int D>
+hipError_t launch_d(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
                     int blocks, size_t lds, const DeviceInfo& dev, hipStream_t stream) {
   static std::atomic<uint64_t> attr_set{0};   // one bit per device
   const uint64_t bit = 1ull << (dev.device & 63);
-  auto kern = gemv_mfma_kernel<M, G, GATED>;
+  auto kern = gemv_mfma_kernel<M, G, GATED, D>;
   if (!(attr_set.load(std::memory_order_acquire) & bit)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)dev.max_lds);
@@ -332,6 +342,18 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* s
   const uint16_t* sc_aligned = reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(scales) - sc_shift);
   return launch_kernel(kern, dim3(blocks), dim3(kThreads), lds, stream, x, packed, sc_aligned, y, n, k,
                        units / blocks, units % blocks, sc_shift);
+}
+
+template <int M, int G, bool GATED>
+hipError_t launch_m(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, uint16_t* y, int n, int k,
+                    int blocks, size_t lds, const DeviceInfo& dev, hipStream_t stream) {
+  // units per wave of the largest workgroup: 8-row blocks x 256-k lines over the waves
+  const int unit = GATED ? 2 : 1;
+  const int per = n / unit;
+  const int rows = unit * (per / blocks + (per % blocks ? 1 : 0));
+  const int upw = ((rows + kRows - 1) / kRows) * ((k + KL - 1) / KL) / kWaves;
+  return upw <= kShallowUnits ? launch_d<M, G, GATED, kShallowDepth>(x, packed, scales, y, n, k, blocks, lds, dev, stream)
+                              : launch_d<M, G, GATED, kDepth>(x, packed, scales, y, n, k, blocks, lds, dev, stream);
 }
 
 template <int M, bool GATED>
