@@ -20,12 +20,14 @@
 //   64 and wraps at the row length, one compare per item.  An item that contains
 //   a row end splits its lanes between the two rows (a wave-uniform test); the
 //   finished row is reduced across lanes at once.
-// * Rows cut between waves are finished without a workgroup barrier: each wave
-//   leaves the wave-reduced partial sums of its first and last row in LDS and
-//   bumps the row's counter; the wave that brings the counter to the number of
-//   contributors adds the partials in wave order (deterministic).  Finished rows
-//   collect in LDS and each wave writes its own to y after its loop, so the
-//   loop itself issues no global stores.
+// * Rows cut between waves: each wave leaves the wave-reduced partial sums of
+//   its first and last row in LDS; after one workgroup barrier, one lane per
+//   wave boundary adds the partials of the row that boundary cuts, in wave
+//   order (deterministic), reading them all at once.  Finished rows collect in
+//   LDS and the whole workgroup writes them to y after a second barrier, so the
+//   loop itself issues no global stores.  (The workgroup cannot end before its
+//   slowest wave anyway; combining after a barrier keeps the slowest wave's
+//   path after its loop to a few LDS round trips.)
 // * The weights come through buffer loads marked non-temporal, issued a fixed
 //   number of items ahead of use.  The item offset goes in the scalar offset
 //   field, so a load costs no vector address arithmetic; loads past the end use
@@ -85,7 +87,7 @@ template <int M>
 struct XSumSlots { static constexpr int value = (M == 1) ? 1 : (M == 2 ? 2 : 4); };
 
 struct GemvLayout {
-  uint32_t xs, sc, part, cnt, res, total;   // byte offsets of the LDS regions, and the size
+  uint32_t xs, sc, part, res, total;   // byte offsets of the LDS regions, and the size
 };
 
 __host__ __device__ inline GemvLayout gemv_layout(int m, int chunks, int spr, int rows_wg) {
@@ -93,15 +95,10 @@ __host__ __device__ inline GemvLayout gemv_layout(int m, int chunks, int spr, in
   l.xs = 0;
   l.sc = (uint32_t)chunks * (uint32_t)(4 * m + 1) * 16u;
   l.part = l.sc + (((uint32_t)rows_wg * (uint32_t)spr * 2u + 15u) & ~15u) + 32u + kScaleSlack;
-  l.cnt = l.part + (uint32_t)(kGemvWaves * 2 * kPartSlots * 4);
-  l.res = l.cnt + (((uint32_t)rows_wg * 4u + 15u) & ~15u);
+  l.res = l.part + (uint32_t)(kGemvWaves * 2 * kPartSlots * 4);
   l.total = l.res + (uint32_t)rows_wg * (uint32_t)m * 4u;
   return l;
 }
-
-// s_waitcnt with only the LDS/scalar counter at zero (vector memory and export
-// counters left at their maxima).
-constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 
 // LDS layout (chunk c = 32 consecutive k of a row):
 //   xs[c] : (4M + 1) slots of 16 bytes: slot 4m + j = for word j of chunk c the
@@ -112,8 +109,7 @@ constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 //           chunks on distinct banks, and one address serves all slots;
 //   sc : a 16-byte-aligned copy of the scales of the workgroup's rows (plus slack);
 //   part[wave][2][4] : partial sums of the first / last row of each wave;
-//   cnt[row] : how many waves have left a partial sum of the row;
-//   res[row][m] : finished fp32 sums, written to y by the wave that finished them.
+//   res[row][m] : finished fp32 sums of the workgroup's rows, written to y at the end.
 template <int M, bool GATED>
 __global__ void __launch_bounds__(kGemvThreads)
 gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
@@ -233,8 +229,6 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   for (uint32_t t = threadIdx.x + kGemvThreads; t < sc_chunks; t += kGemvThreads) {
     *reinterpret_cast<u32x4*>(smem + L.sc + t * 16u) = load16_tail(sres, sc_a0 + t * 16u, sc_bytes);
   }
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + L.cnt);
-  for (int r = threadIdx.x; r < nr; r += kGemvThreads) cnt[r] = 0u;
   __syncthreads();
 
   // ---- main loop over this wave's items ----
@@ -443,71 +437,50 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     flush();
   }
 
-  // ---- rows cut between waves: count this wave in; the last contributor adds the partials ----
-  bool comb_first = false, comb_last = false;    // this wave finished a cut row
-  auto count_in = [&](int r) {
-    // LDS accesses of one wave complete in order, so the partial-slot writes land
-    // before the count; the empty asm statements keep the compiler from moving
-    // LDS accesses across the count.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    uint32_t before = 0;
-    if (lane == 0) before = __hip_atomic_fetch_add(cnt + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    before = __builtin_amdgcn_readfirstlane(before);
-    asm volatile("" ::: "memory");
-    const int start = r * C, end = start + C;
-    int contributors = 0;
+  // ---- rows cut between waves: after one workgroup barrier, one lane per wave
+  // boundary adds the partials of the row that boundary cuts (in wave order) ----
+  __syncthreads();
+  if (threadIdx.x >= 1 && threadIdx.x < kGemvWaves) {
+    const int b = threadIdx.x;                   // boundary between waves b - 1 and b
+    const int cb = bound(b) << 6;                // its block chunk
+    const int r = cb / C;
+    // The row is cut here if the boundary lies strictly inside it; the lane of
+    // the row's first boundary combines it.
+    const bool first_in_row = b == 1 || (bound(b - 1) << 6) <= r * C;
+    if (cb < chunks && cb != r * C && first_in_row) {
+      const int start = r * C, end = start + C;
+      // All slots are read at once (a slot of a wave that has no part of the row
+      // holds an unrelated value and is not added).
+      float pv[kGemvWaves][M];
+      bool in[kGemvWaves];
 #pragma unroll
-    for (int w2 = 0; w2 < kGemvWaves; ++w2) {
-      const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
-      contributors += (a1 > a0 && a0 < end && a1 > start) ? 1 : 0;
-    }
-    if ((int)before != contributors - 1) return false;
-    if (lane < M) {
-      float sum = 0.f;
-  #pragma unroll
-    for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+      for (int w2 = 0; w2 < kGemvWaves; ++w2) {
         const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
-        if (a1 > a0 && a0 < end && a1 > start)
-          sum += parts[w2 * (2 * kPartSlots) + (a0 / C == r ? 0 : kPartSlots) + lane];
+        in[w2] = a1 > a0 && a0 < end && a1 > start;
+        const float* slot = parts + w2 * (2 * kPartSlots) + (a0 / C == r ? 0 : kPartSlots);
+#pragma unroll
+        for (int m = 0; m < M; ++m) pv[w2][m] = slot[m];
       }
-      res[r * M + lane] = sum;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kGemvWaves; ++w2) sum += in[w2] ? pv[w2][m] : 0.f;
+        res[r * M + m] = sum;
+      }
     }
-    return true;
-  };
-  if (cnt_items > 0) {
-    const int c_lo = t0 << 6, c_hi_w = t1 << 6;
-    const int r_last_w = (min(c_hi_w, chunks) - 1) / C;
-    const bool first_cut = !(r_first * C >= c_lo && (r_first + 1) * C <= c_hi_w);
-    const bool last_cut = r_last_w != r_first && !((r_last_w + 1) * C <= c_hi_w);
-    if (first_cut) comb_first = count_in(r_first);
-    if (last_cut) comb_last = count_in(r_last_w);
   }
+  __syncthreads();
 
   if constexpr (GATED) {
-    // Every row of the workgroup is in res once all waves have passed this point.
-    __syncthreads();
     const int pairs_wg = nr >> 1, n_out = n >> 1;
     for (int e = threadIdx.x; e < pairs_wg * M; e += kGemvThreads) {
       const int pr = e / M, m = e - (e / M) * M;
       const float g = res[(2 * pr) * M + m], u = res[(2 * pr + 1) * M + m];
       y[(size_t)m * n_out + (wg_r0 >> 1) + pr] = float_to_half_bits(g / (1.f + __expf(-g)) * u);
     }
-    return;
-  }
-
-  // ---- y for the rows this wave finished: whole rows, and cut rows it combined ----
-  if (cnt_items > 0) {
-    const int c_lo = t0 << 6, c_hi = min(t1 << 6, chunks);
-    const int r_last = (c_hi - 1) / C;
-    const int ra = (c_lo % C == 0) ? r_first : r_first + 1;   // first whole row
-    const int rb = (c_hi % C == 0) ? r_last + 1 : r_last;     // end of whole rows
-    // A combined first row lies just before ra, a combined last row at rb (when
-    // the range lies inside one row, only the first flag can be set).
-    const int p0 = comb_first ? r_first : ra;
-    int p1 = comb_last ? r_last + 1 : rb;
-    if (comb_first && p1 < r_first + 1) p1 = r_first + 1;
-    for (int e = p0 * M + lane; e < p1 * M; e += 64) {
+  } else {
+    for (int e = threadIdx.x; e < nr * M; e += kGemvThreads) {
       const int rl = e / M, m = e - (e / M) * M;
       y[(size_t)m * n + wg_r0 + rl] = float_to_half_bits(res[e]);
     }
