@@ -187,6 +187,28 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 #pragma unroll
   for (int u = 0; u < U; ++u) issue(u);
 
+  // ---- cut-row bookkeeping, done while the first loads are in flight ----
+  // Lane b (1 <= b < waves) of wave 0 adds, after the loop, the partial sums of
+  // the row that the boundary between waves b - 1 and b cuts, if that row is cut
+  // there first.  It records which waves hold a part of the row and which of them
+  // left it in their last-row slot (their range starts before the row).
+  int comb_row = -1;
+  uint32_t comb_in = 0u, comb_last = 0u;
+  if (threadIdx.x >= 1 && threadIdx.x < kGemvWaves) {
+    const int b = threadIdx.x;
+    const int cb = bound(b) << 6;
+    const int start = (cb / C) * C, end = start + C;
+    if (cb < chunks && cb != start && (b == 1 || (bound(b - 1) << 6) <= start)) {
+      comb_row = start / C;
+#pragma unroll
+      for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+        const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
+        if (a1 > a0 && a0 < end && a1 > start) comb_in |= 1u << w2;
+        if (a0 < start) comb_last |= 1u << w2;
+      }
+    }
+  }
+
   // ---- staging: activations regrouped to the nibble pairing, chunk sums, scales ----
   const uint32_t one2 = 0x3C003C00u;  // fp16 pair (1, 1)
   auto stage_pair = [&](int idx, const u32x4 (&v4)[4]) {
@@ -437,37 +459,25 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     flush();
   }
 
-  // ---- rows cut between waves: after one workgroup barrier, one lane per wave
-  // boundary adds the partials of the row that boundary cuts (in wave order) ----
+  // ---- rows cut between waves: after one workgroup barrier, the lanes chosen
+  // above add the partials of their rows in wave order, all slots read at once
+  // (a slot of a wave with no part of the row holds an unrelated value and is
+  // not added) ----
   __syncthreads();
-  if (threadIdx.x >= 1 && threadIdx.x < kGemvWaves) {
-    const int b = threadIdx.x;                   // boundary between waves b - 1 and b
-    const int cb = bound(b) << 6;                // its block chunk
-    const int r = cb / C;
-    // The row is cut here if the boundary lies strictly inside it; the lane of
-    // the row's first boundary combines it.
-    const bool first_in_row = b == 1 || (bound(b - 1) << 6) <= r * C;
-    if (cb < chunks && cb != r * C && first_in_row) {
-      const int start = r * C, end = start + C;
-      // All slots are read at once (a slot of a wave that has no part of the row
-      // holds an unrelated value and is not added).
-      float pv[kGemvWaves][M];
-      bool in[kGemvWaves];
+  if (comb_row >= 0) {
+    float pv[kGemvWaves][M];
 #pragma unroll
-      for (int w2 = 0; w2 < kGemvWaves; ++w2) {
-        const int a0 = bound(w2) << 6, a1 = bound(w2 + 1) << 6;
-        in[w2] = a1 > a0 && a0 < end && a1 > start;
-        const float* slot = parts + w2 * (2 * kPartSlots) + (a0 / C == r ? 0 : kPartSlots);
+    for (int w2 = 0; w2 < kGemvWaves; ++w2) {
+      const float* slot = parts + w2 * (2 * kPartSlots) + (((comb_last >> w2) & 1u) ? kPartSlots : 0);
 #pragma unroll
-        for (int m = 0; m < M; ++m) pv[w2][m] = slot[m];
-      }
+      for (int m = 0; m < M; ++m) pv[w2][m] = slot[m];
+    }
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float sum = 0.f;
+    for (int m = 0; m < M; ++m) {
+      float sum = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < kGemvWaves; ++w2) sum += in[w2] ? pv[w2][m] : 0.f;
-        res[r * M + m] = sum;
-      }
+      for (int w2 = 0; w2 < kGemvWaves; ++w2) sum += ((comb_in >> w2) & 1u) ? pv[w2][m] : 0.f;
+      res[comb_row * M + m] = sum;
     }
   }
   __syncthreads();
