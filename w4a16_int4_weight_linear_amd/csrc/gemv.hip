@@ -209,6 +209,19 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     }
   }
 
+  // ---- loop set-up that needs integer division, also done while the loads are in
+  // flight (the empty asm statements keep the compiler from moving it past the
+  // staging barrier) ----
+  // Lane's chunk in the block: f = 64 t + lane; its chunk in the row, c = f mod C,
+  // addresses the activations; f >> gshift indexes the block's scales.
+  const int f_first = (t0 << 6) + lane;
+  int c_first = f_first % C;
+  int r_first = __builtin_amdgcn_readfirstlane((t0 << 6) / C);   // row of the wave's first chunk
+  // the activation step per item: 64 chunks, or 64 mod C for rows shorter than 64 chunks
+  int x_adv_chunks = __builtin_amdgcn_readfirstlane(C >= 64 ? 64 : 64 % C);
+  asm volatile("" : "+v"(c_first));
+  asm volatile("" : "+s"(r_first), "+s"(x_adv_chunks));
+
   // ---- staging: activations regrouped to the nibble pairing, chunk sums, scales ----
   const uint32_t one2 = 0x3C003C00u;  // fp16 pair (1, 1)
   auto stage_pair = [&](int idx, const u32x4 (&v4)[4]) {
@@ -256,14 +269,10 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   // ---- main loop over this wave's items ----
   float* parts = reinterpret_cast<float*>(smem + L.part);
   float* res = reinterpret_cast<float*>(smem + L.res);
-  // Lane's chunk in the block: f = 64 t + lane; its chunk in the row, c = f mod C,
-  // addresses the activations; f >> gshift indexes the block's scales.
-  const int f_first = (t0 << 6) + lane;
   const uint32_t xs_end = L.xs + (uint32_t)C * kChunkBytes;
   const uint32_t xs_wrap = (uint32_t)C * kChunkBytes;
-  const uint32_t x_step = 64u * kChunkBytes;   // advance by 64 chunks (C >= 64: one wrap at most)
-  // For rows shorter than 64 chunks the step is 64 mod C chunks (whole rows skipped).
-  const uint32_t x_adv = C >= 64 ? x_step : (uint32_t)(64 % C) * kChunkBytes;
+  // advance by 64 chunks (C >= 64: one wrap at most), or 64 mod C (whole rows skipped)
+  const uint32_t x_adv = (uint32_t)x_adv_chunks * kChunkBytes;
   const uint32_t sc_base = L.sc + (sc_begin - sc_a0);
   const uint32_t s_step = (uint32_t)((64 >> gshift) * 2);
   struct Pos {
@@ -325,7 +334,6 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
 
-  const int r_first = (t0 << 6) / C;             // row of the wave's first chunk
   int row = r_first;                             // row of lane 0's chunk
   int row_end = (row + 1) * C;                   // block chunk where that row ends
 
@@ -389,8 +397,7 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   const int cnt_items = t1 - t0;
   Pos cur_pos;
   {
-    const int c0 = f_first % C;
-    cur_pos.xa = L.xs + (uint32_t)c0 * kChunkBytes;
+    cur_pos.xa = L.xs + (uint32_t)c_first * kChunkBytes;
     cur_pos.sa = sc_base + (uint32_t)(f_first >> gshift) * 2u;
   }
   Opnd cur;
