@@ -18,12 +18,18 @@
 //   (With a 16 x 16 product the sixteen columns of one load would be sixteen
 //   rows, 64 bytes each: half lines, which this part reads markedly slower.)
 // * Each lane's 16 bytes (32 k) feed 8 MFMAs of 4 k.  Since 32 divides the
-//   group size, a lane's 32 k lie in one quantisation group: the codes enter
-//   the MFMA as the fp16 values 1024 + u (one mask and two byte permutes per
-//   pair, exact), the 8 MFMAs give t = sum x (1024 + u) over the chunk, and
-//   the scale and the offset are applied once per chunk on the four
-//   accumulators: acc += s * (t - 1032 * sum x).  This is exact for integer
-//   data and the same for every group size.
+//   group size, a lane's 32 k lie in one quantisation group.  The codes enter
+//   the MFMA without conversion instructions: one AND-OR per pair of codes
+//   keeps two nibbles and sets an fp16 exponent above them.  The nibbles of
+//   even k sit at mantissa bits 0-3 and take exponent 2^-10, giving
+//   2^-10 + u 2^-20; those of odd k sit at bits 4-7 and take 2^-14, giving
+//   2^-14 + 16 u 2^-24 = 2^-14 + u 2^-20: the same weight for u, exact, five
+//   instructions per packed word.  The 8 MFMAs give t over the chunk; the
+//   activations' biased sum b = sum x_even (2^-10 + 8 2^-20) + sum x_odd
+//   (2^-14 + 8 2^-20) is staged per chunk, so t - b = 2^-20 sum x (u - 8),
+//   and the scale is applied once per chunk on the four accumulators:
+//   acc += s (t - b); the 2^20 is restored when a row is finished.  This is
+//   exact for integer data and the same for every group size.
 // * Work split: each workgroup (one per CU) owns a contiguous range of weight
 //   rows (sizes differ by at most one row), covered by 8-row blocks.  Its units
 //   (block, line) are dealt to the waves as contiguous runs in block-major
@@ -31,7 +37,7 @@
 //   like the M = 1 kernel's flat streams.
 // * The activations are staged in LDS once per workgroup, each group of 8 k in
 //   the order the dequantisation produces (k = 0, 4, 2, 6, 1, 5, 3, 7), with
-//   the sum of every 32-k chunk per row; the workgroup's scales are staged
+//   the biased sum b of every 32-k chunk per row; the workgroup's scales are staged
 //   beside them.  Lanes whose A row is not a real activation row read row
 //   i mod M, whose results are never stored.
 // * When a wave leaves a block, the eight lanes holding the chunks of one row
@@ -103,17 +109,11 @@ __host__ __device__ inline Layout lds_layout(int m, int k, int spr, int rows) {
   return l;
 }
 
-// The eight codes of packed word q as the fp16 values 1024 + u, in the order
-// (0, 4), (2, 6), (1, 5), (3, 7) of dequant_word (exact; no offset, no scale).
-__device__ inline u32x4 codes_1024(uint32_t q) {
-  const uint32_t magic = 0x64646464u;
-  const uint32_t qa = q & 0x0F0F0F0Fu;            // bytes u0 u2 u4 u6
-  const uint32_t qb = (q >> 4) & 0x0F0F0F0Fu;     // bytes u1 u3 u5 u7
-  return u32x4{__builtin_amdgcn_perm(magic, qa, 0x04020400u), __builtin_amdgcn_perm(magic, qa, 0x04030401u),
-               __builtin_amdgcn_perm(magic, qb, 0x04020400u), __builtin_amdgcn_perm(magic, qb, 0x04030401u)};
-}
-
 __device__ inline f16x4 as_h4(uint32_t a, uint32_t b) { return __builtin_bit_cast(f16x4, u32x2{a, b}); }
+
+// fp16 pair (2^-10 + 8 2^-20, 2^-14 + 8 2^-20): the code bias plus 8 code units, for the
+// (even k, odd k) activations of a pair
+constexpr uint32_t kBiasPair = 0x04801408u;
 
 // rows_base / rows_extra count row units: single rows, or (gate, up) row pairs
 // (GATED).  `scales` is rounded down to 16 bytes by the launcher and sc_shift
@@ -209,11 +209,10 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
             *reinterpret_cast<u32x4*>(smem + L.xs + (uint32_t)m * xp + 16u * (uint32_t)c) = permute_a(v[h][m]);
           // the 32-k sum over 4 chunks, which are 4 consecutive lanes (one DPP quad;
           // chunks per row are a multiple of 4 and so is the thread count)
-          const uint32_t one2 = 0x3C003C00u;   // fp16 pair (1, 1)
-          float sum = dot2(v[h][m].x, one2, 0.f);
-          sum = dot2(v[h][m].y, one2, sum);
-          sum = dot2(v[h][m].z, one2, sum);
-          sum = dot2(v[h][m].w, one2, sum);
+          float sum = dot2(v[h][m].x, kBiasPair, 0.f);
+          sum = dot2(v[h][m].y, kBiasPair, sum);
+          sum = dot2(v[h][m].z, kBiasPair, sum);
+          sum = dot2(v[h][m].w, kBiasPair, sum);
           sum = dpp_add<0xB1>(sum);    // quad_perm [1,0,3,2]
           sum = dpp_add<0x4E>(sum);    // quad_perm [2,3,0,1]
           if (c < chunks && (c & 3) == 0) reinterpret_cast<float*>(smem + L.xsum)[(c >> 2) * 4 + m] = sum;
@@ -246,11 +245,15 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
       float t = dpp_add<0x124>(v[i]);   // row_ror:4
       t = dpp_add<0x128>(t);            // row_ror:8
       t += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));   // lane ^ 16
-      v[i] = t;
+      v[i] = t * 0x1p20f;
     }
     if (lc == 0) reinterpret_cast<f32x4*>(smem + L.red)[(wave * nb + b) * kRows + lr] = v;
     acc = f32x4{};
   };
+  // Masks and exponents in registers, so each pair of codes is one v_and_or_b32.
+  const uint32_t m_lo = __builtin_amdgcn_readfirstlane(0x000F000Fu), m_hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
+  uint32_t e_even = 0x14001400u, e_odd = 0x04000400u;   // fp16 exponent fields 5 and 1, both halves
+  asm volatile("" : "+v"(e_even), "+v"(e_odd));
   auto consume = [&](const u32x4& wv) {
     const uint8_t* xs = xa + 512u * (uint32_t)s;
     u32x4 xf[4];
@@ -260,9 +263,12 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
-      const u32x4 c = codes_1024(q);
-      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].x, xf[w].y), as_h4(c.x, c.y), t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].z, xf[w].w), as_h4(c.z, c.w), t, 0, 0, 0);
+      const uint32_t q8 = q >> 8;
+      // even k (0, 4), (2, 6) with x pairs (0, 4), (2, 6); odd k (1, 5), (3, 7) likewise
+      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].x, xf[w].y),
+                                             as_h4((q & m_lo) | e_even, (q8 & m_lo) | e_even), t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].z, xf[w].w),
+                                             as_h4((q & m_hi) | e_odd, (q8 & m_hi) | e_odd), t, 0, 0, 0);
     }
     // the lane's chunk is one group; rows past the workgroup's range and chunks
     // past K (zero weights) take scale 0
@@ -272,7 +278,7 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
         ok ? half_bits_to_float(*reinterpret_cast<const uint16_t*>(scb + 2u * ((uint32_t)(kRows * b * spr) + kc / G))) : 0.f;
     const f32x4 xsum = *reinterpret_cast<const f32x4*>(xsa + 128u * (uint32_t)s);
 #pragma unroll
-    for (int i = 0; i < M; ++i) acc[i] = __builtin_fmaf(sc, __builtin_fmaf(-1032.f, xsum[i], t[i]), acc[i]);
+    for (int i = 0; i < M; ++i) acc[i] = __builtin_fmaf(sc, t[i] - xsum[i], acc[i]);
     if (++s == lines) {
       flush();
       s = 0;
