@@ -159,7 +159,7 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   // Every slot is loaded unconditionally, in a fixed order, so the compiler can
   // wait for each load alone (vmcnt); a load past the wave's units has an
   // out-of-range offset and a zero scalar offset: it touches no memory.
-  auto issue = [&](int slot) {
+  auto issue = [&](int slot) __attribute__((always_inline)) {
     const bool live = iu < u1;
     const uint32_t voff = !live ? kOutOfRange : (is == lines - 1 ? w_v_tail : w_v);
     ring[slot] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -231,13 +231,13 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   // A operand: activation row li mod M, the lane's chunk (lanes of other rows read the same addresses)
   const uint8_t* xa = smem + L.xs + (uint32_t)(li % M) * xp + 64u * (uint32_t)lc;
   const uint8_t* xsa = smem + L.xsum + 16u * (uint32_t)lc;
-  // this lane's scales: row lr of each block
-  const uint8_t* scb = smem + L.sc + (((uint32_t)r0 * (uint32_t)spr * 2u + sc_shift) & 15u) + 2u * (uint32_t)(lr * spr);
+  // the workgroup's scales (row-major, spr per row)
+  const uint8_t* scb = smem + L.sc + (((uint32_t)r0 * (uint32_t)spr * 2u + sc_shift) & 15u);
   f32x4 acc = f32x4{};
   // consume cursor (b, s); a block's partial sums go to LDS after its last
   // line, or at the end if the wave stops inside the block
   int b = b_first, s = s_first;
-  auto flush = [&]() {
+  auto flush = [&]() __attribute__((always_inline)) {
     // add the eight chunk lanes of each row: lane bits 2, 3 (DPP), then bit 4
     f32x4 v = acc;
 #pragma unroll
@@ -254,37 +254,54 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   const uint32_t m_lo = __builtin_amdgcn_readfirstlane(0x000F000Fu), m_hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
   uint32_t e_even = 0x14001400u, e_odd = 0x04000400u;   // fp16 exponent fields 5 and 1, both halves
   asm volatile("" : "+v"(e_even), "+v"(e_odd));
-  auto consume = [&](const u32x4& wv) {
-    const uint8_t* xs = xa + 512u * (uint32_t)s;
+  // The LDS operands of a unit: the lane's activations and chunk sums, and its
+  // scale -- 0 for rows past the workgroup's range and chunks past K (zero
+  // weights), read from a clamped, valid address so the read is unconditional.
+  struct Opnd {
     u32x4 xf[4];
+    f32x4 xsum;
+    float sc;
+  };
+  auto read_opnd = [&](int bb, int ss, Opnd& o) __attribute__((always_inline)) {
+    const uint8_t* xs = xa + 512u * (uint32_t)ss;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) xf[w] = *reinterpret_cast<const u32x4*>(xs + 16 * w);
+    for (int w = 0; w < 4; ++w) o.xf[w] = *reinterpret_cast<const u32x4*>(xs + 16 * w);
+    o.xsum = *reinterpret_cast<const f32x4*>(xsa + 128u * (uint32_t)ss);
+    const int row = kRows * bb + lr;
+    const uint32_t kc = (uint32_t)(KL * ss + 32 * lc);
+    const bool ok = row < nr && kc < (uint32_t)K;
+    const uint32_t idx = ok ? (uint32_t)row * (uint32_t)spr + kc / G : 0u;
+    const float v = half_bits_to_float(*reinterpret_cast<const uint16_t*>(scb + 2u * idx));
+    o.sc = ok ? v : 0.f;
+  };
+  Opnd cur;
+  read_opnd(b, s, cur);
+  // One unit: the next unit's LDS operands are read before this one's arithmetic.
+  auto consume = [&](const u32x4& wv) __attribute__((always_inline)) {
+    const bool last_line = s + 1 == lines;
+    Opnd nxt;
+    read_opnd(last_line ? b + 1 : b, last_line ? 0 : s + 1, nxt);
     f32x4 t = f32x4{};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
       const uint32_t q8 = q >> 8;
       // even k (0, 4), (2, 6) with x pairs (0, 4), (2, 6); odd k (1, 5), (3, 7) likewise
-      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].x, xf[w].y),
+      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(cur.xf[w].x, cur.xf[w].y),
                                              as_h4((q & m_lo) | e_even, (q8 & m_lo) | e_even), t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(xf[w].z, xf[w].w),
+      t = __builtin_amdgcn_mfma_f32_4x4x4f16(as_h4(cur.xf[w].z, cur.xf[w].w),
                                              as_h4((q & m_hi) | e_odd, (q8 & m_hi) | e_odd), t, 0, 0, 0);
     }
-    // the lane's chunk is one group; rows past the workgroup's range and chunks
-    // past K (zero weights) take scale 0
-    const uint32_t kc = (uint32_t)(KL * s + 32 * lc);
-    const bool ok = lr < nr - kRows * b && kc < (uint32_t)K;
-    const float sc =
-        ok ? half_bits_to_float(*reinterpret_cast<const uint16_t*>(scb + 2u * ((uint32_t)(kRows * b * spr) + kc / G))) : 0.f;
-    const f32x4 xsum = *reinterpret_cast<const f32x4*>(xsa + 128u * (uint32_t)s);
 #pragma unroll
-    for (int i = 0; i < M; ++i) acc[i] = __builtin_fmaf(sc, t[i] - xsum[i], acc[i]);
-    if (++s == lines) {
-      flush();
-      s = 0;
-      ++b;
-    }
+    for (int i = 0; i < M; ++i) acc[i] = __builtin_fmaf(cur.sc, t[i] - cur.xsum[i], acc[i]);
+    if (last_line) flush();
+    b += last_line ? 1 : 0;
+    s = last_line ? 0 : s + 1;
+    cur = nxt;
   };
+  // The wave's last units run through the same loop (a wave-uniform test skips
+  // the slots past its end; their loads are out of range and touch no memory),
+  // so no separate straight-line tail is fetched cold while the stream drains.
   int u = u0;
   for (; u + D <= u1; u += D) {
 #pragma unroll
