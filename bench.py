@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--stream-counter-table", nargs="+", metavar="ARG",
                     help="OUT_MD COMMAND CSV [CSV ...]: per-workload SQ/TCP counters of the weight-streaming "
                          "kernels from one or more --pmc passes (host only, no GPU)")
+    ap.add_argument("--wave-timeline", metavar="OUT_MD",
+                    help="run the decode workloads and the read probe on the profiling library "
+                         "(stamps/libw4a16.so, per-wave timeline stamps) and write the per-wave "
+                         "timeline breakdown to OUT_MD")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "COMMAND"),
                     help="turn a rocprofv3 kernel trace of this benchmark into the per-kernel "
                          "summaries profiles/*.kernel_trace.md (host only, no GPU)")
@@ -896,6 +900,142 @@ def stream_counter_table(csv_paths, out_md, command):
     print("wrote", out_md)
 
 
+# ---------------------------------------------------------------------------
+# Per-wave timelines (profiling library with wave stamps).
+# ---------------------------------------------------------------------------
+STAMP_SLOTS = 8
+STAMP_NAMES = (("start", 0), ("staged", 1), ("first unit", 2), ("loop end", 3), ("end barrier", 4), ("end", 5))
+STAMP_NS = 10.0        # the real-time counter runs at 100 MHz
+
+
+def timeline_stats(stamps):
+    """stamps: [launches, 256 workgroups, 8 waves, STAMP_SLOTS] counter values (0 = not
+    recorded).  For every slot, per launch: the mean and the max over waves of the time
+    since the launch's first wave started (ns); returned as medians over launches, with
+    the derived phases: the loop (mean loop end - mean first unit), the tail (max - mean
+    loop end) and the span (max end)."""
+    a = np.asarray(stamps, dtype=np.int64)
+    t0 = a[:, :, :, 0].min(axis=(1, 2))[:, None, None]
+    out = {}
+    for name, i in STAMP_NAMES:
+        v = a[:, :, :, i]
+        if not np.any(v):
+            continue
+        d = (v - t0).astype(np.float64) * STAMP_NS
+        d[v == 0] = np.nan
+        out[name] = {"mean": float(np.median(np.nanmean(d, axis=(1, 2)))),
+                     "max": float(np.median(np.nanmax(d, axis=(1, 2))))}
+    if "first unit" in out and "loop end" in out:
+        out["loop"] = out["loop end"]["mean"] - out["first unit"]["mean"]
+        out["tail"] = out["loop end"]["max"] - out["loop end"]["mean"]
+    out["span"] = out["end"]["max"]
+    return out
+
+
+def timeline_table(results, command, out_md):
+    """results: {workload: (stats, graph per-launch us, probe workload name)}."""
+    lines = ["Commands (from the repository root on the GPU box), then the summary:", "", "```", command, "```", "",
+             "Profiling library stamps/libw4a16.so (same kernels, plus per-wave 100 MHz real-time stamps kept in "
+             "registers and stored once at the end).  Each workload: a HIP graph of 10 launches over rotating "
+             "weight copies (>= 1 GiB, so every launch reads HBM), replayed 30 times; the stamps of the last "
+             "launch of each replay; times in us since that launch's first wave started, medians over the 30 "
+             "launches of the mean and the max over the 2048 recorded waves.  'first unit' = the wave's first "
+             "1 KiB of weights consumed (for the probe: arrived); 'staged' = activations, sums and scales in LDS "
+             "(workgroup barrier passed); per launch = graph time / launches (includes the gap between "
+             "launches, which no stamp sees).", "",
+             "| workload | per launch | start mean / max | staged mean / max | first unit mean / max | "
+             "loop end mean / max | end mean / max | loop | tail | first unit - probe's | loop - probe's | "
+             "span - probe's |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    us = lambda v: f"{v / 1000:.2f}"
+    mm = lambda st, k: f"{us(st[k]['mean'])} / {us(st[k]['max'])}" if k in st else "-"
+    for name, (st, launch_us, ref) in results.items():
+        p = results[ref][0] if ref else None
+        dfirst = us(st["first unit"]["mean"] - p["first unit"]["mean"]) if p and "first unit" in st else "-"
+        dloop = us(st["loop"] - p["loop"]) if p and "loop" in st else "-"
+        dspan = us(st["span"] - p["span"]) if p else "-"
+        lines.append(f"| {name} | {launch_us:.2f} | {mm(st, 'start')} | {mm(st, 'staged')} | {mm(st, 'first unit')} | "
+                     f"{mm(st, 'loop end')} | {mm(st, 'end')} | {us(st['loop']) if 'loop' in st else '-'} | "
+                     f"{us(st['tail']) if 'tail' in st else '-'} | {dfirst} | {dloop} | {dspan} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def wave_timeline(torch, w4, out_md):
+    import ctypes
+    path = os.path.join(ROOT, "w4a16_int4_weight_linear_amd", "stamps", "libw4a16.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it first (python -m w4a16_int4_weight_linear_amd.build)")
+    slib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    for fn, (res, argt) in w4.SIGNATURES.items():
+        f = getattr(slib, fn)
+        f.restype = res
+        f.argtypes = argt
+    acc = {}
+    for key in ("gemv", "gemv_mfma", "probe"):
+        f = getattr(slib, f"w4a16_wave_stamps_{key}")
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        acc[key] = f
+    product_lib = w4.lib
+    w4.lib = slib            # the binding calls through the profiling library meanwhile
+    torch.manual_seed(0)
+    launches, replays = 10, 30
+
+    def pool_of(n, k, g=128):
+        per = n * k // 2 + n * (k // g) * 2
+        copies = max(3, -(-POOL_BYTES // per))
+        return [(torch.randint(-2 ** 31, 2 ** 31 - 1, (n, k // 8), dtype=torch.int32, device="cuda"),
+                 (torch.rand((n, k // g), device="cuda") * 0.01).half()) for _ in range(copies)]
+
+    def run(fn, key):
+        g = _graph_of(torch, fn, launches)
+        if g is None:
+            raise RuntimeError("graph capture failed")
+        g.replay()
+        torch.cuda.synchronize()
+        buf = np.zeros((replays, 256, 8, STAMP_SLOTS), dtype=np.uint64)
+        ms = []
+        for r in range(replays):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            g.replay()
+            s1.record()
+            torch.cuda.synchronize()
+            ms.append(s0.elapsed_time(s1))
+            if acc[key](buf[r].ctypes.data_as(ctypes.c_void_p), buf[r].nbytes) != 0:
+                raise RuntimeError("stamp read-back failed")
+        return timeline_stats(buf), float(np.median(ms)) * 1e3 / launches
+
+    results = {}
+    try:
+        probe_name = "HBM read probe, 46,001,152 B (one decode launch's bytes)"
+        for name, (m, n, k, ref) in {
+                "M=1 decode up 5120->17408": (1, 17408, 5120, probe_name),
+                "M=1 decode down 17408->5120": (1, 5120, 17408, probe_name),
+                "M=4 batched decode N=17408 (np4)": (4, 17408, 5120, probe_name),
+                "M=4 batched decode N=5120 (np4)": (4, 5120, 5120, None)}.items():
+            pool = pool_of(n, k)
+            x = torch.randn((m, k), device="cuda").half()
+            y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+            st, lu = run(lambda i: w4.gemv(x, *pool[i % len(pool)], 128, out=y), "gemv" if m == 1 else "gemv_mfma")
+            results[name] = (st, lu, ref)
+            print(f"timeline: {name} {lu:.2f} us per launch", file=sys.stderr, flush=True)
+            del pool
+            torch.cuda.empty_cache()
+        nbytes = (dense_bytes(1, 17408, 5120, 128) // 1024) * 1024
+        flat = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(max(3, -(-POOL_BYTES // nbytes)))]
+        sink = torch.empty(slib.w4a16_hbm_read_probe_sink_words(), dtype=torch.int32, device="cuda")
+        st, lu = run(lambda i: w4.hbm_read_probe(flat[i % len(flat)], sink), "probe")
+        results = {probe_name: (st, lu, None), **results}
+        print(f"timeline: probe {lu:.2f} us per launch", file=sys.stderr, flush=True)
+    finally:
+        w4.lib = product_lib
+    command = ("cd <repo>; python3 -c 'import __graft_entry__ as g; g.build()'   # on the build host\n"
+               f"python3 bench.py --wave-timeline {os.path.relpath(out_md, ROOT)}")
+    timeline_table(results, command, out_md)
+
+
 XCDS = 8   # MI355X: GRBM counters are reported once per XCD and summed by the profiler
 
 
@@ -1165,6 +1305,9 @@ def main():
         sys.exit(1)
     import synth
     import w4a16_int4_weight_linear_amd as w4
+    if args.wave_timeline:
+        wave_timeline(torch, w4, args.wave_timeline)
+        return
 
     if args.traffic_probe:
         traffic_probe(torch, w4, synth)

@@ -4,6 +4,8 @@ when asked for more, and its trace summariser labels every workload."""
 import json
 import os
 import subprocess
+
+import numpy as np
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -176,3 +178,36 @@ def test_gemm_counter_summary_ratios(tmp_path):
     assert by["M=4096"][5] == "0.600"
     vendor = [v for k, v in by.items() if k.startswith("Cijk_")]
     assert len(vendor) == 1 and vendor[0][5] == "0.500"
+
+
+def test_wave_timeline_stats_and_table(tmp_path):
+    """Synthetic stamps (10 ns ticks): workgroups start 0.1 us apart by index modulo 4,
+    stage at +1 us, finish their first unit at +1.5 us, their loop at +6 us (+7 us for
+    wave 7) and end 0.5 us later; unrecorded slots are zero."""
+    bench = _bench()
+    launches = 3
+    a = np.zeros((launches, 256, 8, bench.STAMP_SLOTS), np.uint64)
+    base = 1_000_000
+    for r in range(launches):
+        for b in range(256):
+            for w in range(8):
+                t = base + r * 100_000 + (b % 4) * 10
+                loop_end = t + (700 if w == 7 else 600)
+                a[r, b, w, :6] = [t, t + 100, t + 150, loop_end, loop_end + 20, loop_end + 50]
+    st = bench.timeline_stats(a)
+    assert st["start"]["max"] == 300.0 and abs(st["start"]["mean"] - 150.0) < 1e-9
+    assert st["first unit"]["max"] == 1800.0
+    assert abs(st["loop"] - 4625.0) < 1e-9          # mean loop end 6275 (one wave in eight at +7 us) - 1650
+    assert st["loop end"]["max"] == 7300.0 and st["span"] == 7800.0
+    probe = np.zeros_like(a)
+    probe[:, :, :, 0] = a[:, :, :, 0]
+    probe[:, :, :, 2] = a[:, :, :, 0] + 120
+    probe[:, :, :, 3] = a[:, :, :, 0] + 580
+    probe[:, :, :, 5] = a[:, :, :, 0] + 600
+    sp = bench.timeline_stats(probe)
+    assert "staged" not in sp and sp["span"] == 6300.0
+    out = tmp_path / "t.md"
+    bench.timeline_table({"probe": (sp, 8.8, None), "gemv": (st, 10.5, "probe")}, "cmd", str(out))
+    row = [ln for ln in out.read_text().splitlines() if ln.startswith("| gemv")][0]
+    cells = [c.strip() for c in row.split("|")[1:-1]]
+    assert cells[1] == "10.50" and cells[11] == "1.50"      # span 7.8 us against the probe's 6.3 us

@@ -3,6 +3,12 @@
 Every HIP source is compiled for gfx950 only; the host-only sources are
 compiled by the same driver.  Objects go to _build/ at the repository root and
 the shared library next to this file, where the binding loads it.
+
+A second, profiling-only library is built from the same sources with
+-DW4A16_WAVE_STAMPS into stamps/libw4a16.so: its weight-streaming kernels also
+record per-wave timeline stamps (csrc/wave_stamps.hpp), read back through the
+extern "C" accessors w4a16_wave_stamps_gemv / _gemv_mfma / _probe, which only
+that library exports.  The binding never loads it; bench.py --wave-timeline does.
 """
 
 from __future__ import annotations
@@ -18,6 +24,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
+STAMPS_LIB = os.path.join(PKG, "stamps", "libw4a16.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -39,9 +46,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(hipcc: str, src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *HIP_FLAGS, "-c", src, "-o", obj]
+def _compile(hipcc: str, src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc, *HIP_FLAGS, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-Wall", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,23 +68,33 @@ def _check_resolves(path: str) -> None:
         raise RuntimeError(f"linked library does not load: {r.stderr.strip().splitlines()[-1] if r.stderr else ''}")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libw4a16.so; returns the library path."""
-    hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+def _build_one(hipcc: str, lib: str, build_dir: str, extra, verbose: bool) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(hipcc, s, build_dir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     _check_resolves(tmp)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources", file=sys.stderr)
+    return lib
+
+
+def build(verbose: bool = False, wave_stamps: bool = True) -> str:
+    """Compile every source and link libw4a16.so (and, unless wave_stamps is
+    False, the profiling library stamps/libw4a16.so); returns the product
+    library's path."""
+    hipcc = _hipcc()
+    lib = _build_one(hipcc, LIB, BUILD, (), verbose)
+    if wave_stamps:
+        _build_one(hipcc, STAMPS_LIB, os.path.join(BUILD, "stamps"), ("-DW4A16_WAVE_STAMPS",), verbose)
+    return lib
 
 
 if __name__ == "__main__":

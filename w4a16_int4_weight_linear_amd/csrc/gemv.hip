@@ -61,6 +61,9 @@
 #include "device.hpp"
 #include "kernels.hpp"
 #include "launch.hpp"
+#include "wave_stamps.hpp"
+
+W4A16_STAMP_STORAGE(w4a16_wave_stamps_gemv)
 
 namespace w4a16 {
 namespace {
@@ -130,6 +133,10 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   const int lane = threadIdx.x & 63;
   // wave index, made explicitly wave-uniform so the bookkeeping lives in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // timeline stamps (profiling build only; the M = 1 decode kernel)
+  constexpr bool kStamped = M == 1 && !GATED;
+  W4A16_STAMP_DECL;
+  if (kStamped) W4A16_STAMP(0);
   const int blk = blockIdx.x;
   const int nr = kUnit * (rows_base + (blk < rows_extra ? 1 : 0));       // rows of this workgroup
   const int wg_r0 = kUnit * (blk * rows_base + (blk < rows_extra ? blk : rows_extra));
@@ -265,6 +272,7 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     *reinterpret_cast<u32x4*>(smem + L.sc + t * 16u) = load16_tail(sres, sc_a0 + t * 16u, sc_bytes);
   }
   __syncthreads();
+  if (kStamped) W4A16_STAMP(1);
 
   // ---- main loop over this wave's items ----
   float* parts = reinterpret_cast<float*>(smem + L.part);
@@ -451,6 +459,7 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (base + u < cnt_items) consume(u, base + u);
+      if (kStamped && base == 0 && u == 0) W4A16_STAMP(2);
       issue(u);
     }
   }
@@ -466,11 +475,13 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     flush();
   }
 
+  if (kStamped) W4A16_STAMP(3);
   // ---- rows cut between waves: after one workgroup barrier, the lanes chosen
   // above add the partials of their rows in wave order, all slots read at once
   // (a slot of a wave with no part of the row holds an unrelated value and is
   // not added) ----
   __syncthreads();
+  if (kStamped) W4A16_STAMP(4);
   if (comb_row >= 0) {
     float pv[kGemvWaves][M];
 #pragma unroll
@@ -501,6 +512,10 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
       const int rl = e / M, m = e - (e / M) * M;
       y[(size_t)m * n + wg_r0 + rl] = float_to_half_bits(res[e]);
     }
+  }
+  if (kStamped) {
+    W4A16_STAMP(5);
+    W4A16_STAMP_FLUSH(wave);
   }
 }
 

@@ -56,6 +56,9 @@
 #include "kernels.hpp"
 #include "launch.hpp"
 #include "mfma_operands.hpp"
+#include "wave_stamps.hpp"
+
+W4A16_STAMP_STORAGE(w4a16_wave_stamps_gemv_mfma)
 
 namespace w4a16 {
 namespace {
@@ -128,6 +131,10 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // timeline stamps (profiling build only; the four-row, non-gated kernel)
+  constexpr bool kStamped = M == 4 && !GATED;
+  W4A16_STAMP_DECL;
+  if (kStamped) W4A16_STAMP(0);
   const int lr = (lane & 3) + 4 * (lane >> 5);    // weight row of the block (B column)
   const int lc = (lane >> 2) & 7;                 // 32-k chunk of the line
   const int li = lane & 3;                        // A row of the 4 x 4 block
@@ -226,6 +233,7 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
       reinterpret_cast<f32x4*>(smem + L.red)[t] = f32x4{};
   }
   __syncthreads();
+  if (kStamped) W4A16_STAMP(1);
 
   // ---- main loop over this wave's units ----
   // A operand: activation row li mod M, the lane's chunk (lanes of other rows read the same addresses)
@@ -299,14 +307,14 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
     s = last_line ? 0 : s + 1;
     cur = nxt;
   };
-  // The wave's last units run through the same loop (a wave-uniform test skips
-  // the slots past its end; their loads are out of range and touch no memory),
-  // so no separate straight-line tail is fetched cold while the stream drains.
+  // Whole rounds of D units, then the wave's last units (fewer than D) after the
+  // loop (for this kernel measured faster than skipping slots inside the loop).
   int u = u0;
   for (; u + D <= u1; u += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       consume(ring[d]);
+      if (kStamped && d == 0 && u == u0) W4A16_STAMP(2);
       issue(d);
     }
   }
@@ -314,9 +322,11 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   for (int d = 0; d < D; ++d)
     if (u + d < u1) consume(ring[d]);
   if (s != 0) flush();
+  if (kStamped) W4A16_STAMP(3);
 
   // ---- add the waves' partials in wave order, round once, store ----
   __syncthreads();
+  if (kStamped) W4A16_STAMP(4);
   const f32x4* red = reinterpret_cast<const f32x4*>(smem + L.red);
   if constexpr (GATED) {
     // rows (2i, 2i + 1) of a block are one (gate, up) pair
@@ -345,6 +355,10 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
         for (int m = 0; m < M; ++m) y[(size_t)m * N + r0 + row] = float_to_half_bits(v[m]);
       }
     }
+  }
+  if (kStamped) {
+    W4A16_STAMP(5);
+    W4A16_STAMP_FLUSH(wave);
   }
 }
 

@@ -12,6 +12,9 @@
 #include "device.hpp"
 #include "kernels.hpp"
 #include "launch.hpp"
+#include "wave_stamps.hpp"
+
+W4A16_STAMP_STORAGE(w4a16_wave_stamps_probe)
 
 namespace w4a16 {
 namespace {
@@ -24,6 +27,8 @@ __global__ void __launch_bounds__(kProbeThreads)
 stream_read_kernel(const uint8_t* __restrict__ buf, uint64_t items, uint32_t* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  W4A16_STAMP_DECL;   // timeline stamps (profiling build only)
+  W4A16_STAMP(0);
   // items (1 KiB each) of this workgroup, then of this wave
   const uint64_t g0 = items * blockIdx.x / gridDim.x, g1 = items * (blockIdx.x + 1) / gridDim.x;
   const uint64_t w0 = g0 + (g1 - g0) * wave / kProbeWaves, w1 = g0 + (g1 - g0) * (wave + 1) / kProbeWaves;
@@ -41,16 +46,25 @@ stream_read_kernel(const uint8_t* __restrict__ buf, uint64_t items, uint32_t* __
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
       acc ^= v[u];
+#ifdef W4A16_WAVE_STAMPS
+      if (u == 0 && i == 0) {
+        asm volatile("" ::"v"(acc.x));   // the first item has arrived
+        W4A16_STAMP(2);
+      }
+#endif
       const uint32_t nx = i + kInFlight + (uint32_t)u;
       v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
           r, voff, nx < n ? nx << 10 : kOutOfRange, kStream));
     }
   }
+  W4A16_STAMP(3);
   uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   // fold the wave's lanes (any order: XOR)
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) x ^= (uint32_t)__shfl_xor((int)x, d);
   if (lane == 0) sink[blockIdx.x * kProbeWaves + wave] = x;
+  W4A16_STAMP(5);
+  W4A16_STAMP_FLUSH(wave);
 }
 
 }  // namespace
