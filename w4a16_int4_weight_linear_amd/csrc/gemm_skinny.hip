@@ -121,31 +121,51 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
     return __builtin_amdgcn_raw_buffer_load_b16(sres, off, 0, 0);
   };
 
-  // ---- unit order: chunk by chunk; inside chunk c, unit j -> (block j % nb, line 8 c + j / nb) ----
-  auto chunk_units = [&](int c) { return nb * min(kChunkLines, lines - kChunkLines * c); };
+  // ---- unit order: chunk by chunk; inside chunk c, unit j -> (block j % nb, line 8 c + j / nb),
+  // units j = wave, wave + 8, ... to this wave.  The cursor (chunk, block, line in chunk) advances
+  // by additions only: j + 8 is block + 8 % nb, line + 8 / nb, with a carry (no division per unit).
+  auto chunk_lines = [&](int c) { return min(kChunkLines, lines - kChunkLines * c); };
+  const int b0 = wave % nb, l0 = wave / nb;         // the wave's first unit of every chunk
+  const int db = kWaves % nb, dl = kWaves / nb;
+  struct Cursor {
+    int c, b, l, lc;                                // chunk, block, line in the chunk, lines in the chunk
+  };
+  // the wave's first unit in chunk u.c or a later one (u.c == chunks: none left)
+  auto first_unit = [&](Cursor& u) {
+    for (; u.c < chunks; ++u.c) {
+      u.lc = chunk_lines(u.c);
+      u.b = b0;
+      u.l = l0;
+      if (l0 < u.lc) return;
+    }
+  };
+  auto next_unit = [&](Cursor& u) {
+    u.b += db;
+    u.l += dl;
+    if (u.b >= nb) {
+      u.b -= nb;
+      ++u.l;
+    }
+    if (u.l >= u.lc) {
+      ++u.c;
+      first_unit(u);
+    }
+  };
   struct Slot {
     u32x4 raw[2];
     u32x4 s32;
     uint32_t s128;
     uint32_t s16[2];
   };
-  auto issue = [&](int c, int j, Slot& sl) {
-    const bool ok = c < chunks;
-    const int b = ok ? j % nb : 0;
-    const int s = ok ? kChunkLines * c + j / nb : lines;   // past the end: no memory access
+  auto issue = [&](const Cursor& u, Slot& sl) {
+    const bool ok = u.c < chunks;
+    const int b = ok ? u.b : 0;
+    const int s = ok ? kChunkLines * u.c + u.l : lines;   // past the end: no memory access
     sl.raw[0] = load_raw(b, s, 0);
     sl.raw[1] = load_raw(b, s, 1);
     if constexpr (ALIGNED && G == 32) sl.s32 = load_s32(b, s);
     if constexpr (ALIGNED && G == 128) sl.s128 = load_s128(b, s);
     if constexpr (!ALIGNED) { sl.s16[0] = load_s16(b, s, 0); sl.s16[1] = load_s16(b, s, 1); }
-  };
-  // the unit after (c, j) for this wave: j + 8 in the chunk, else its first unit of a later chunk
-  auto next_unit = [&](int& c, int& j) {
-    j += kWaves;
-    while (c < chunks && j >= chunk_units(c)) {
-      ++c;
-      j = wave;
-    }
   };
 
   // ---- activation chunks: thread -> row tid / 32, pieces (tid % 32) + 32 p ----
@@ -167,9 +187,9 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
   };
 
   Slot sl;
-  int uc = 0, uj = wave;                            // this wave's next unit to issue
-  if (uj >= chunk_units(0)) next_unit(uc, uj);
-  issue(uc, uj, sl);
+  Cursor iu = {0, 0, 0, 0};                         // this wave's next unit to issue
+  first_unit(iu);
+  issue(iu, sl);
   u32x4 xv[kXPieces];
   load_x(0, xv);
   store_x(0, xv);
@@ -184,11 +204,11 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
 
   // One unit in flight per wave (a second one measured no faster).
   for (int c = 0; c < chunks; ++c) {
-    const int cu = chunk_units(c);
     const uint8_t* xc = xfrag + (c & 1) * kXBuf;
-    for (int j = wave; j < cu; j += kWaves) {
-      const int b = j % nb;
-      const int sl_line = j / nb;                   // line within the chunk
+    Cursor cu = {c, b0, l0, chunk_lines(c)};        // this wave's units of chunk c
+    for (; cu.l < cu.lc; cu.b += db, cu.l += dl, cu.b >= nb ? (cu.b -= nb, ++cu.l) : 0) {
+      const int b = cu.b;
+      const int sl_line = cu.l;                     // line within the chunk
       *reinterpret_cast<u32x4*>(tile_w) = sl.raw[0];
       *reinterpret_cast<u32x4*>(tile_w + 1024) = sl.raw[1];
       const u32x4 wq0 = *reinterpret_cast<const u32x4*>(tile_r0);
@@ -206,8 +226,8 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
           sv[h] = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(sl.s128, sl.s128, h ? 0x03020302u : 0x01000100u));
         }
       }
-      next_unit(uc, uj);
-      issue(uc, uj, sl);                            // the wave's next unit (past the end: no memory access)
+      next_unit(iu);
+      issue(iu, sl);                                // the wave's next unit (past the end: no memory access)
       const uint8_t* xb = xc + 512 * sl_line;
       f32x4 part = f32x4{};
 #pragma unroll
