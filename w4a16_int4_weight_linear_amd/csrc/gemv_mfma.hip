@@ -177,61 +177,74 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
       ++ib;
     }
   };
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(d);
-
   // ---- stage the activations (and their 32-k sums), the scales, zero partials ----
-  {
-    // chunk c of row m: 8 k, stored permuted; 4 consecutive chunks (lanes) are one 32-k sum
-    const int chunks = lines * (KL / 8);
-    const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-    // scales of the workgroup's rows, 16-byte chunks from an aligned start; the
-    // first chunk of each thread is loaded here, under the activation loads
-    const uint32_t sc_begin = (uint32_t)r0 * (uint32_t)spr * 2u + sc_shift;
-    const uint32_t sc_a0 = sc_begin & ~15u;
-    const uint32_t sc_bytes = (uint32_t)N * (uint32_t)spr * 2u + sc_shift;
-    const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, sc_bytes);
-    const uint32_t sc_chunks = (sc_begin - sc_a0 + (uint32_t)nr * (uint32_t)spr * 2u + 15u) >> 4;
-    u32x4 sc_first = u32x4{};
-    if ((uint32_t)tid < sc_chunks) sc_first = load16_tail(sres, sc_a0 + (uint32_t)tid * 16u, sc_bytes);
-    // thread tid takes chunks c0 + tid and c0 + tid + kThreads of every row: 2 M
-    // loads in flight, no index division
-    for (int c0 = 0; c0 < chunks; c0 += 2 * kThreads) {
-      u32x4 v[2][M];
+  // chunk c of row m: 8 k, stored permuted; 4 consecutive chunks (lanes) are one 32-k sum
+  const int chunks = lines * (KL / 8);
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  // scales of the workgroup's rows, 16-byte chunks from an aligned start
+  const uint32_t sc_begin = (uint32_t)r0 * (uint32_t)spr * 2u + sc_shift;
+  const uint32_t sc_a0 = sc_begin & ~15u;
+  const uint32_t sc_bytes = (uint32_t)N * (uint32_t)spr * 2u + sc_shift;
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc(scales, sc_bytes);
+  const uint32_t sc_chunks = (sc_begin - sc_a0 + (uint32_t)nr * (uint32_t)spr * 2u + 15u) >> 4;
+  // thread tid takes chunks c0 + tid and c0 + tid + kThreads of every row: 2 M
+  // loads in flight, no index division
+  u32x4 sv[2][M];
+  auto load_stage = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = c0 + h * kThreads + tid;
-        const bool ok = c < chunks && 8 * c < K;
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + h * kThreads + tid;
+      const bool ok = c < chunks && 8 * c < K;
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-          v[h][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-              xres, ok ? ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)c) * 2u : kOutOfRange, 0, 0));
-      }
+      for (int m = 0; m < M; ++m)
+        sv[h][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            xres, ok ? ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)c) * 2u : kOutOfRange, 0, 0));
+    }
+  };
+  auto store_stage = [&](int c0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = c0 + h * kThreads + tid;
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + h * kThreads + tid;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          if (c < chunks)
-            *reinterpret_cast<u32x4*>(smem + L.xs + (uint32_t)m * xp + 16u * (uint32_t)c) = permute_a(v[h][m]);
-          // the 32-k sum over 4 chunks, which are 4 consecutive lanes (one DPP quad;
-          // chunks per row are a multiple of 4 and so is the thread count)
-          float sum = dot2(v[h][m].x, kBiasPair, 0.f);
-          sum = dot2(v[h][m].y, kBiasPair, sum);
-          sum = dot2(v[h][m].z, kBiasPair, sum);
-          sum = dot2(v[h][m].w, kBiasPair, sum);
-          sum = dpp_add<0xB1>(sum);    // quad_perm [1,0,3,2]
-          sum = dpp_add<0x4E>(sum);    // quad_perm [2,3,0,1]
-          if (c < chunks && (c & 3) == 0) reinterpret_cast<float*>(smem + L.xsum)[(c >> 2) * 4 + m] = sum;
-        }
+      for (int m = 0; m < M; ++m) {
+        if (c < chunks)
+          *reinterpret_cast<u32x4*>(smem + L.xs + (uint32_t)m * xp + 16u * (uint32_t)c) = permute_a(sv[h][m]);
+        // the 32-k sum over 4 chunks, which are 4 consecutive lanes (one DPP quad;
+        // chunks per row are a multiple of 4 and so is the thread count)
+        float sum = dot2(sv[h][m].x, kBiasPair, 0.f);
+        sum = dot2(sv[h][m].y, kBiasPair, sum);
+        sum = dot2(sv[h][m].z, kBiasPair, sum);
+        sum = dot2(sv[h][m].w, kBiasPair, sum);
+        sum = dpp_add<0xB1>(sum);    // quad_perm [1,0,3,2]
+        sum = dpp_add<0x4E>(sum);    // quad_perm [2,3,0,1]
+        if (c < chunks && (c & 3) == 0) reinterpret_cast<float*>(smem + L.xsum)[(c >> 2) * 4 + m] = sum;
       }
     }
-    if ((uint32_t)tid < sc_chunks) *reinterpret_cast<u32x4*>(smem + L.sc + (uint32_t)tid * 16u) = sc_first;
-    for (uint32_t t = tid + kThreads; t < sc_chunks; t += kThreads)
-      *reinterpret_cast<u32x4*>(smem + L.sc + t * 16u) = load16_tail(sres, sc_a0 + t * 16u, sc_bytes);
-    for (uint32_t t = tid; t < (uint32_t)(kWaves * nb * kRows); t += kThreads)
-      reinterpret_cast<f32x4*>(smem + L.red)[t] = f32x4{};
+  };
+  // A long stream (the deep ring) issues the first activation and scale loads
+  // before its first weight loads, a short one after them (measured both ways).
+  constexpr bool kStageFirst = D > kShallowDepth;
+  if constexpr (!kStageFirst) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d);
   }
+  u32x4 sc_first = u32x4{};
+  if ((uint32_t)tid < sc_chunks) sc_first = load16_tail(sres, sc_a0 + (uint32_t)tid * 16u, sc_bytes);
+  load_stage(0);
+  if constexpr (kStageFirst) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d);
+  }
+  store_stage(0);
+  for (int c0 = 2 * kThreads; c0 < chunks; c0 += 2 * kThreads) {
+    load_stage(c0);
+    store_stage(c0);
+  }
+  if ((uint32_t)tid < sc_chunks) *reinterpret_cast<u32x4*>(smem + L.sc + (uint32_t)tid * 16u) = sc_first;
+  for (uint32_t t = tid + kThreads; t < sc_chunks; t += kThreads)
+    *reinterpret_cast<u32x4*>(smem + L.sc + t * 16u) = load16_tail(sres, sc_a0 + t * 16u, sc_bytes);
+  for (uint32_t t = tid; t < (uint32_t)(kWaves * nb * kRows); t += kThreads)
+    reinterpret_cast<f32x4*>(smem + L.red)[t] = f32x4{};
   __syncthreads();
   if (kStamped) W4A16_STAMP(1);
 
