@@ -78,6 +78,9 @@ namespace {
 #ifndef W4A16_NP4_WG_PER_CU
 #define W4A16_NP4_WG_PER_CU 1
 #endif
+#ifndef W4A16_NP4_SKEW
+#define W4A16_NP4_SKEW 100
+#endif
 constexpr int kThreads = W4A16_NP4_THREADS;
 constexpr int kWaves = kThreads / 64;
 // Loads in flight per wave: a wave with few units (a small launch) does better
@@ -85,6 +88,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kDepth = W4A16_NP4_LOADS_IN_FLIGHT;
 constexpr int kShallowDepth = W4A16_NP4_SHALLOW_LOADS;
 constexpr int kShallowUnits = W4A16_NP4_SHALLOW_UNITS;   // units per wave at or below which it is used
+constexpr int kSkew = W4A16_NP4_SKEW;           // in 1/1024: extra share of the older wave of each SIMD
 constexpr int KL = 256;                         // k per line: 128 bytes of a weight row
 constexpr int kRows = 8;                        // weight rows per block (one load)
 constexpr int kMaxBlocks = 32;                  // blocks per workgroup
@@ -150,7 +154,15 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
   const uint32_t xp = x_pitch(K);
 
   // ---- this wave's units [u0, u1) and its first loads ----
-  const int u0 = (int)((int64_t)units * wave / kWaves), u1 = (int)((int64_t)units * (wave + 1) / kWaves);
+  // Waves 0 .. kWaves/2 - 1 are the older wave of their SIMD and issue first:
+  // they take a share 1 + skew of the units, the younger half 1 - skew.
+  auto bound = [&](int w) {
+    constexpr int kHalf = kWaves / 2;
+    const int64_t cum = w <= kHalf ? (int64_t)w * (1024 + kSkew)
+                                   : (int64_t)kHalf * (1024 + kSkew) + (int64_t)(w - kHalf) * (1024 - kSkew);
+    return (int)(cum * units / (kWaves * 1024));
+  };
+  const int u0 = bound(wave), u1 = bound(wave + 1);
   const uint32_t row_w = (uint32_t)K >> 1;
   // the descriptor covers exactly the workgroup's rows: rows past its range read zero
   const __amdgpu_buffer_rsrc_t wres =
