@@ -700,7 +700,11 @@ def _split_runs(d, n):
 
 
 def _family(short):
-    return next((b for b in TRACE_FILES if short.startswith(b)), None)
+    """The family of a kernel's short name: the family key itself, or the key with
+    further template arguments (e.g. a ring depth: "f<4, 128, false, 4>" is family
+    "f<4, 128, false>")."""
+    return next((b for b in TRACE_FILES
+                 if short.startswith(b) or (b.endswith(">") and short.startswith(b[:-1] + ","))), None)
 
 
 def _label_runs(base, items):
@@ -809,6 +813,7 @@ def _algorithmic_rw(base, label):
         ("gemv_mfma_kernel<4, 128, false>", "N=17408"): rw(4, 17408, 5120, 128),
         ("gemv_kernel<1, true>", "M=1, gate+up 5120->2x17408 (SwiGLU)"): rw(1, 2 * 17408, 5120, 128),
         ("gemv_mfma_kernel<4, 128, true>", "M=4, gate+up 5120->2x17408 (SwiGLU)"): rw(4, 2 * 17408, 5120, 128),
+        ("gemm_skinny_kernel", "M=16, up 5120->17408 (batched decode)"): rw(16, 17408, 5120, 128),
     }
     r = table.get((base, label))
     if r is not None and "SwiGLU" in label:

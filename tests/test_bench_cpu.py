@@ -114,12 +114,14 @@ def test_traffic_table_scales_by_the_copy_calibration(tmp_path):
     prof = tmp_path / "profiles"
     prof.mkdir()
     (prof / "gemv.traffic.json").write_text(json.dumps({"fetch_scale": 2.0, "write_scale": 1.0}))
-    np4 = "void w4a16::(anonymous namespace)::gemv_mfma_kernel<4, 128, false>(int)"
+    # the two workloads run kernels of one family with different ring depths
+    np4 = ["void w4a16::(anonymous namespace)::gemv_mfma_kernel<4, 128, false, 3>(int)",
+           "void w4a16::(anonymous namespace)::gemv_mfma_kernel<4, 128, false, 4>(int)"]
     fetch, write, t = [], [], 0
     for r, (kib_read, kib_write) in enumerate(((6000.0, 40.0), (20000.0, 136.0))):
         for _ in range(3):
-            fetch.append((np4, 131072, t, 1000, {"FETCH_SIZE": kib_read}))
-            write.append((np4, 131072, t, 1000, {"WRITE_SIZE": kib_write}))
+            fetch.append((np4[r], 131072, t, 1000, {"FETCH_SIZE": kib_read}))
+            write.append((np4[r], 131072, t, 1000, {"WRITE_SIZE": kib_write}))
             t += 2000
         t += 10_000_000
     _write_counters(tmp_path / "f.csv", fetch)
