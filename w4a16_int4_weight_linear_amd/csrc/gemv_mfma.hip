@@ -34,7 +34,8 @@
 //   rows (sizes differ by at most one row), covered by 8-row blocks.  Its units
 //   (block, line) are dealt to the waves as contiguous runs in block-major
 //   order, so every wave streams along its rows with several loads in flight,
-//   like the M = 1 kernel's flat streams.
+//   like the M = 1 kernel's flat streams.  The older wave of each SIMD, whose
+//   loads are issued first, takes a slightly larger run.
 // * The activations are staged in LDS once per workgroup, each group of 8 k in
 //   the order the dequantisation produces (k = 0, 4, 2, 6, 1, 5, 3, 7), with
 //   the biased sum b of every 32-k chunk per row; the workgroup's scales are staged
