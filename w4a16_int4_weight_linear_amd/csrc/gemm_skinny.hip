@@ -46,7 +46,10 @@ constexpr int kXBuf = kRows * kXPitch;
 constexpr int kXPieces = kRows * KCH / 8 / kThreads;   // 16-byte pieces per thread and chunk
 constexpr int kTileWave = 16 * 128;
 constexpr int kTileBase = 2 * kXBuf;
-constexpr int kLds = kTileBase + kWaves * kTileWave;
+constexpr int kGroupsPerChunk = KCH / 128;        // 128-k groups per staged chunk
+constexpr int kXSumBuf = kRows * kGroupsPerChunk * 4;   // biased activation sums of one chunk (g128 path)
+constexpr int kXSumBase = kTileBase + kWaves * kTileWave;
+constexpr int kLds = kXSumBase + 2 * kXSumBuf;
 static_assert(kXPieces == 8, "staging assumes eight pieces per thread");
 static_assert(kLds <= 160 * 1024, "LDS");
 static_assert(kWaves * kMaxBlocks * 1024 <= kLds, "the final partial tiles reuse the LDS");
@@ -65,6 +68,12 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane >> 4;
   const int li = lane & 15;
+  // Group 128 with aligned scales: every MFMA's 32 k lie in one group (k =
+  // 128 h + 32 lq + 8 w + j for MFMA (h, w)), so the codes enter it without
+  // conversion (one AND-OR per pair, see kBiasPair) and the scale is applied once
+  // per group to the MFMA results; otherwise each word is dequantised with its
+  // scale before the MFMA.
+  constexpr bool kEnc = G == 128 && ALIGNED;
 
   // rows_base / rows_extra count whole rows, or whole (gate, up) row pairs
   constexpr int kUnit = SWIGLU ? 2 : 1;
@@ -184,6 +193,23 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
     uint8_t* dst = smem + (c & 1) * kXBuf + xr * kXPitch + xq * 16;
 #pragma unroll
     for (int p = 0; p < kXPieces; ++p) *reinterpret_cast<u32x4*>(dst + 512 * p) = permute_a(v[p]);
+    if constexpr (kEnc) {
+      // the biased sum of every 128-k group of the row: its 16 pieces are one
+      // 16-lane DPP row (pieces xq + 32 p, xq = lane mod 32)
+      float* xs = reinterpret_cast<float*>(smem + kXSumBase + (c & 1) * kXSumBuf) + xr * kGroupsPerChunk;
+#pragma unroll
+      for (int p = 0; p < kXPieces; ++p) {
+        float t = dot2(v[p].x, kBiasPair, 0.f);
+        t = dot2(v[p].y, kBiasPair, t);
+        t = dot2(v[p].z, kBiasPair, t);
+        t = dot2(v[p].w, kBiasPair, t);
+        t = dpp_add<0xB1>(t);    // quad_perm [1,0,3,2]
+        t = dpp_add<0x4E>(t);    // quad_perm [2,3,0,1]
+        t = dpp_add<0x124>(t);   // row_ror:4
+        t = dpp_add<0x128>(t);   // row_ror:8
+        if ((xq & 15) == 0) xs[2 * p + (xq >> 4)] = t;
+      }
+    }
   };
 
   Slot sl;
@@ -201,10 +227,15 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
   for (int b = 0; b < kMaxBlocks; ++b) acc[b] = f32x4{};
   const uint32_t sel_lq = (uint32_t)(2 * lq) * 0x00010001u + (uint32_t)(2 * lq + 1) * 0x01000100u;
   const uint8_t* xfrag = smem + li * kXPitch + 64 * lq;
+  // encoded path: masks and exponents in registers, so each pair of codes is one v_and_or_b32
+  const uint32_t m_lo = __builtin_amdgcn_readfirstlane(0x000F000Fu), m_hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
+  uint32_t e_even = 0x14001400u, e_odd = 0x04000400u;   // fp16 exponent fields 5 and 1, both halves
+  asm volatile("" : "+v"(e_even), "+v"(e_odd));
 
   // One unit in flight per wave (a second one measured no faster).
   for (int c = 0; c < chunks; ++c) {
     const uint8_t* xc = xfrag + (c & 1) * kXBuf;
+    const uint8_t* xsc = smem + kXSumBase + (c & 1) * kXSumBuf;   // biased sums of chunk c
     Cursor cu = {c, b0, l0, chunk_lines(c)};        // this wave's units of chunk c
     for (; cu.l < cu.lc; cu.b += db, cu.l += dl, cu.b >= nb ? (cu.b -= nb, ++cu.l) : 0) {
       const int b = cu.b;
@@ -213,6 +244,13 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
       *reinterpret_cast<u32x4*>(tile_w + 1024) = sl.raw[1];
       const u32x4 wq0 = *reinterpret_cast<const u32x4*>(tile_r0);
       const u32x4 wq1 = *reinterpret_cast<const u32x4*>(tile_r1);
+      // encoded path: the scales (groups 2 s, 2 s + 1) of the lane's output rows
+      // 4 lq + r, held by lanes 4 lq + r (each lane loaded its operand row li's)
+      uint32_t srow[4];
+      if constexpr (kEnc) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) srow[r] = (uint32_t)__shfl((int)sl.s128, 4 * lq + r);
+      }
       f16x2 sv[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -230,14 +268,39 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
       issue(iu, sl);                                // the wave's next unit (past the end: no memory access)
       const uint8_t* xb = xc + 512 * sl_line;
       f32x4 part = f32x4{};
+      if constexpr (kEnc) {
+        // the biased sums of the lane's activation row li for the line's two groups
+        const float2 bsum = *reinterpret_cast<const float2*>(xsc + li * (kGroupsPerChunk * 4) + 8 * sl_line);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 wv = h ? wq1 : wq0;
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 wv = h ? wq1 : wq0;
+          f32x4 t = f32x4{};
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(xb + 256 * h + 16 * w));
-          const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
-          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(q, sv[h]), xf, part, 0, 0, 0);
+          for (int w = 0; w < 4; ++w) {
+            const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(xb + 256 * h + 16 * w));
+            const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
+            const uint32_t q8 = q >> 8;
+            // pairs (0,4), (2,6), (1,5), (3,7): the activations' slice order
+            const u32x4 a = u32x4{(q & m_lo) | e_even, (q8 & m_lo) | e_even, (q & m_hi) | e_odd, (q8 & m_hi) | e_odd};
+            t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), xf, t, 0, 0, 0);
+          }
+          const float b = h ? bsum.y : bsum.x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float s = half_bits_to_float(h ? srow[r] >> 16 : srow[r] & 0xFFFFu);
+            part[r] = __builtin_fmaf(s, t[r] - b, part[r]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 wv = h ? wq1 : wq0;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f16x8 xf = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(xb + 256 * h + 16 * w));
+            const uint32_t q = w == 0 ? wv.x : (w == 1 ? wv.y : (w == 2 ? wv.z : wv.w));
+            part = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_word(q, sv[h]), xf, part, 0, 0, 0);
+          }
         }
       }
 #pragma unroll
@@ -261,6 +324,7 @@ gemm_skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ 
   if (wave < nb && li < M) {
     f32x4 t = red[wave * 64 + lane];
     for (int w = 1; w < kWaves; ++w) t += red[(w * kMaxBlocks + wave) * 64 + lane];
+    if constexpr (kEnc) t *= 0x1p20f;    // the codes' 2^-20
     // lane holds weight rows 4 lq .. 4 lq + 3 of block `wave` for activation row li
     if constexpr (SWIGLU) {
       // rows r0 + rr (gate) and r0 + rr + 1 (up) for even rr: output (r0 + rr) / 2

@@ -119,10 +119,6 @@ __host__ __device__ inline Layout lds_layout(int m, int k, int spr, int rows) {
 
 __device__ inline f16x4 as_h4(uint32_t a, uint32_t b) { return __builtin_bit_cast(f16x4, u32x2{a, b}); }
 
-// fp16 pair (2^-10 + 8 2^-20, 2^-14 + 8 2^-20): the code bias plus 8 code units, for the
-// (even k, odd k) activations of a pair
-constexpr uint32_t kBiasPair = 0x04801408u;
-
 // rows_base / rows_extra count row units: single rows, or (gate, up) row pairs
 // (GATED).  `scales` is rounded down to 16 bytes by the launcher and sc_shift
 // bytes added back here, so the 16-byte staging loads are aligned in memory.

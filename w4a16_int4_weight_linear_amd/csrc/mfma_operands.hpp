@@ -59,6 +59,16 @@ __device__ inline f16x8 dequant_word_natural(uint32_t q, f16x2 s2) {
   return out;
 }
 
+// Codes without conversion instructions (the batched decode kernels): one AND-OR
+// per pair keeps two nibbles of a packed word and sets an fp16 exponent above
+// them.  The nibbles of even k (mantissa bits 0-3, exponent field 5) read
+// 2^-10 + u 2^-20; those of odd k (bits 4-7, exponent field 1) read
+// 2^-14 + 16 u 2^-24 = 2^-14 + u 2^-20, so each code is u 2^-20 above a per-k
+// bias, exact.  Subtracting the activations' biased sum b = sum x_even (2^-10 +
+// 8 2^-20) + sum x_odd (2^-14 + 8 2^-20) from the product leaves
+// 2^-20 sum x (u - 8).  kBiasPair is that (even k, odd k) fp16 pair.
+constexpr uint32_t kBiasPair = 0x04801408u;
+
 // Eight activations (pairs (0,1),(2,3),(4,5),(6,7)) rearranged into the same
 // slice order: pairs (0,4), (2,6), (1,5), (3,7).
 __device__ inline u32x4 permute_a(u32x4 v) {
