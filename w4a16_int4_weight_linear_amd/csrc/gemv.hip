@@ -226,8 +226,12 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   int r_first = __builtin_amdgcn_readfirstlane((t0 << 6) / C);   // row of the wave's first chunk
   // the activation step per item: 64 chunks, or 64 mod C for rows shorter than 64 chunks
   int x_adv_chunks = __builtin_amdgcn_readfirstlane(C >= 64 ? 64 : 64 % C);
+  // rows [whole_lo, whole_hi) lie wholly inside this wave's items (written to y by
+  // the wave itself after its loop)
+  int whole_lo = __builtin_amdgcn_readfirstlane(((t0 << 6) + C - 1) / C);
+  int whole_hi = __builtin_amdgcn_readfirstlane(min((t1 << 6) / C, nr));
   asm volatile("" : "+v"(c_first));
-  asm volatile("" : "+s"(r_first), "+s"(x_adv_chunks));
+  asm volatile("" : "+s"(r_first), "+s"(x_adv_chunks), "+s"(whole_lo), "+s"(whole_hi));
 
   // ---- staging: activations regrouped to the nibble pairing, chunk sums, scales ----
   const uint32_t one2 = 0x3C003C00u;  // fp16 pair (1, 1)
@@ -476,10 +480,18 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
   }
 
   if (kStamped) W4A16_STAMP(3);
+  // ---- the wave's whole rows go to y now (the loop left them in res; no
+  // global store is issued inside the loop) ----
+  if constexpr (!GATED) {
+    for (int e = lane; e < (whole_hi - whole_lo) * M; e += 64) {
+      const int rl = whole_lo + e / M, m = e - (e / M) * M;
+      y[(size_t)m * n + wg_r0 + rl] = float_to_half_bits(res[rl * M + m]);
+    }
+  }
   // ---- rows cut between waves: after one workgroup barrier, the lanes chosen
   // above add the partials of their rows in wave order, all slots read at once
   // (a slot of a wave with no part of the row holds an unrelated value and is
-  // not added) ----
+  // not added), and store them ----
   __syncthreads();
   if (kStamped) W4A16_STAMP(4);
   if (comb_row >= 0) {
@@ -495,22 +507,22 @@ gemv_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
       float sum = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < kGemvWaves; ++w2) sum += ((comb_in >> w2) & 1u) ? pv[w2][m] : 0.f;
-      res[comb_row * M + m] = sum;
+      if constexpr (GATED) {
+        res[comb_row * M + m] = sum;
+      } else {
+        y[(size_t)m * n + wg_r0 + comb_row] = float_to_half_bits(sum);
+      }
     }
   }
-  __syncthreads();
 
   if constexpr (GATED) {
+    // a (gate, up) pair may have one row cut and the other whole: all rows in res first
+    __syncthreads();
     const int pairs_wg = nr >> 1, n_out = n >> 1;
     for (int e = threadIdx.x; e < pairs_wg * M; e += kGemvThreads) {
       const int pr = e / M, m = e - (e / M) * M;
       const float g = res[(2 * pr) * M + m], u = res[(2 * pr + 1) * M + m];
       y[(size_t)m * n_out + (wg_r0 >> 1) + pr] = float_to_half_bits(g / (1.f + __expf(-g)) * u);
-    }
-  } else {
-    for (int e = threadIdx.x; e < nr * M; e += kGemvThreads) {
-      const int rl = e / M, m = e - (e / M) * M;
-      y[(size_t)m * n + wg_r0 + rl] = float_to_half_bits(res[e]);
     }
   }
   if (kStamped) {
