@@ -230,20 +230,14 @@ gemv_mfma_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ pa
       }
     }
   };
-  // A long stream (the deep ring) issues the first activation and scale loads
-  // before its first weight loads, a short one after them (measured both ways).
-  constexpr bool kStageFirst = D > kShallowDepth;
-  if constexpr (!kStageFirst) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue(d);
-  }
+  // The first activation and scale loads go out before the first weight loads, so
+  // the staging does not wait behind them (measured faster for short and long
+  // streams alike).
   u32x4 sc_first = u32x4{};
   if ((uint32_t)tid < sc_chunks) sc_first = load16_tail(sres, sc_a0 + (uint32_t)tid * 16u, sc_bytes);
   load_stage(0);
-  if constexpr (kStageFirst) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(d);
-  }
+  for (int d = 0; d < D; ++d) issue(d);
   store_stage(0);
   for (int c0 = 2 * kThreads; c0 < chunks; c0 += 2 * kThreads) {
     load_stage(c0);
